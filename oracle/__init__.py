@@ -1,0 +1,7 @@
+"""CPU float64 oracle for exact attention -- TEST INFRASTRUCTURE ONLY.
+
+Only tests/, the smoke check in __graft_entry__.py and bench.py's CPU-baseline
+leg may import this package. The HIP library and its Python binding never do.
+"""
+from .attention import (allowed_matrix, backward, forward, forward_rows, head_backward,  # noqa: F401
+                        head_forward, head_probabilities)

@@ -1,0 +1,149 @@
+"""Standard (exact) attention in float64 on the CPU: the oracle.
+
+TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the bench's
+CPU-baseline leg may import or call this module; the HIP library never does,
+and nothing here is shared with it.
+
+What it computes, per (batch, head) instance with Q, K, V in R^{N x d}:
+  S = scale * Q K^T, P = row-wise softmax(S), O = P V
+  -- FlashAttention reading notes (hackmd), §Background › Standard Attention
+  Implementation, the S / P / O equations. The pages write S = Q K^T; the
+  caller's scale multiplies S (a reading: the workloads use 1/sqrt(d)).
+Masking sets disallowed entries of S to -inf before the softmax (the fused
+kernel there runs "matmul, softmax, masking/dropout, matmul"; the order is read
+as mask-before-softmax so that masked keys get zero probability):
+  * causal: key j is allowed for query i iff j <= i;
+  * key padding: keys j >= key_len[b] are masked for every query of batch b;
+  * block-sparse: entry (i, j) is allowed iff block_mask[i // bs, j // bs] != 0
+    (same notes, §Introduction › Block-sparse FlashAttention: zero blocks are
+    skipped, i.e. they contribute nothing to the softmax).
+A row with no allowed key has P = 0, O = 0 and LSE = -inf (a reading; the
+pages never reach such a row).
+
+The forward also returns LSE = m + ln(l) with m the row max and l the row sum
+of exp(S - m): the pages' forward saves O, m and l (§Algorithm › Recomputation);
+one log-sum-exp per row carries the same information.
+
+The backward is the exact gradient of L = <dO, O> by the chain rule through the
+three equations above (the pages defer it to the paper's appendix):
+  dV = P^T dO,  dP = dO V^T,  D_i = sum_j P_ij dP_ij,
+  dS = P o (dP - D 1^T),  dQ = scale * dS K,  dK = scale * dS^T Q.
+It recomputes P from Q and K; it never uses any LSE produced elsewhere.
+
+Pins (tests/test_oracle.py): hand-solved N=2 and N=4 cases (tests/golden/),
+row sums, closed forms (scale 0, N 1, causal row 0), reductions of every mask
+to plain attention on a sub-range, shift invariances, central finite
+differences of <dO, O>, gradient invariants and an independent library routine
+(torch CPU float64 scaled_dot_product_attention with autograd).
+"""
+from __future__ import annotations
+
+from typing import Iterable, Optional
+
+import numpy as np
+
+
+def allowed_matrix(N: int, causal: bool = False, key_len: Optional[int] = None,
+                   block_mask: Optional[np.ndarray] = None, block_size: Optional[int] = None,
+                   rows: Optional[np.ndarray] = None) -> np.ndarray:
+    """Boolean [len(rows), N]: entry (i, j) is True iff key j may be attended by query rows[i]."""
+    r = np.arange(N) if rows is None else np.asarray(rows)
+    j = np.arange(N)
+    ok = np.ones((r.size, N), dtype=bool)
+    if causal:
+        ok &= j[None, :] <= r[:, None]
+    if key_len is not None:
+        L = min(max(int(key_len), 0), N)
+        ok &= j[None, :] < L
+    if block_mask is not None:
+        bs = int(block_size)
+        ok &= np.asarray(block_mask)[r[:, None] // bs, j[None, :] // bs] != 0
+    return ok
+
+
+def head_probabilities(q: np.ndarray, k: np.ndarray, scale: float, allowed: np.ndarray):
+    """S, P and LSE for one head (float64). q: [R, d] query rows, k: [N, d]."""
+    s = float(scale) * (q @ k.T)
+    s = np.where(allowed, s, -np.inf)
+    m = s.max(axis=1)                       # row max; -inf for a row with no allowed key
+    empty = ~np.isfinite(m)
+    m_safe = np.where(empty, 0.0, m)
+    e = np.exp(s - m_safe[:, None])         # exp(-inf) = 0 on masked entries
+    l = e.sum(axis=1)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        p = np.where(empty[:, None], 0.0, e / np.where(empty, 1.0, l)[:, None])
+        lse = np.where(empty, -np.inf, m_safe + np.log(np.where(empty, 1.0, l)))
+    return s, p, lse
+
+
+def head_forward(q, k, v, scale, allowed):
+    """O and LSE for one head: O = P V."""
+    _, p, lse = head_probabilities(q, k, scale, allowed)
+    return p @ v, lse
+
+
+def head_backward(q, k, v, do, scale, allowed):
+    """dQ, dK, dV for one head, the gradient of <dO, O>; also returns D = rowsum(P o dP)."""
+    _, p, _ = head_probabilities(q, k, scale, allowed)
+    dv = p.T @ do
+    dp = do @ v.T
+    dsum = (p * dp).sum(axis=1)
+    ds = p * (dp - dsum[:, None])
+    dq = float(scale) * (ds @ k)
+    dk = float(scale) * (ds.T @ q)
+    return dq, dk, dv, dsum
+
+
+def _f64(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64)
+
+
+def _heads(B: int, H: int, heads: Optional[Iterable]) -> list:
+    if heads is None:
+        return [(b, h) for b in range(B) for h in range(H)]
+    return [tuple(x) for x in heads]
+
+
+def forward(Q, K, V, scale, causal=False, key_len=None, block_mask=None, block_size=None,
+            heads=None):
+    """Exact attention forward over [B, H, N, d] inputs.
+
+    Returns O [B, H, N, d] and LSE [B, H, N] in float64. With `heads` (a list of
+    (b, h)) only those instances are computed; the rest of the outputs are NaN.
+    """
+    B, H, N, d = Q.shape
+    O = np.full((B, H, N, d), np.nan)
+    LSE = np.full((B, H, N), np.nan)
+    for b, h in _heads(B, H, heads):
+        L = None if key_len is None else int(key_len[b])
+        ok = allowed_matrix(N, causal, L, block_mask, block_size)
+        O[b, h], LSE[b, h] = head_forward(_f64(Q[b, h]), _f64(K[b, h]), _f64(V[b, h]), scale, ok)
+    return O, LSE
+
+
+def forward_rows(Q, K, V, scale, b, h, rows, causal=False, key_len=None, block_mask=None,
+                 block_size=None):
+    """O and LSE of selected query rows of one instance (each row depends only on its own q)."""
+    N = Q.shape[2]
+    rows = np.asarray(rows)
+    L = None if key_len is None else int(key_len[b])
+    ok = allowed_matrix(N, causal, L, block_mask, block_size, rows=rows)
+    return head_forward(_f64(Q[b, h][rows]), _f64(K[b, h]), _f64(V[b, h]), scale, ok)
+
+
+def backward(Q, K, V, dO, scale, causal=False, key_len=None, block_mask=None, block_size=None,
+             heads=None):
+    """Exact gradients dQ, dK, dV [B, H, N, d] (float64) of <dO, O>.
+
+    With `heads` only those instances are computed; the rest are NaN.
+    """
+    B, H, N, d = Q.shape
+    dQ = np.full((B, H, N, d), np.nan)
+    dK = np.full((B, H, N, d), np.nan)
+    dV = np.full((B, H, N, d), np.nan)
+    for b, h in _heads(B, H, heads):
+        L = None if key_len is None else int(key_len[b])
+        ok = allowed_matrix(N, causal, L, block_mask, block_size)
+        dQ[b, h], dK[b, h], dV[b, h], _ = head_backward(
+            _f64(Q[b, h]), _f64(K[b, h]), _f64(V[b, h]), _f64(dO[b, h]), scale, ok)
+    return dQ, dK, dV
