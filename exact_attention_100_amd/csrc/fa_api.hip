@@ -1,0 +1,325 @@
+// The C ABI of include/fa.h: argument checks, workspace carving and dispatch.
+// No device memory is allocated here; every buffer comes from the caller.
+#include <math.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "fa.h"
+#include "fa_internal.hpp"
+
+namespace fa {
+
+// ------------------------------------------------------------------------------ timer
+
+namespace {
+constexpr int kTimerSlots = 8192;
+struct TimerSlot {
+  const char* name;
+  int used;
+};
+struct Timer {
+  std::mutex mu;
+  bool enabled = false;
+  bool created = false;
+  hipEvent_t start[kTimerSlots];
+  hipEvent_t stop[kTimerSlots];
+  TimerSlot slot[kTimerSlots];
+  int n = 0;
+  int open = -1;  // slot whose start event was recorded and whose stop is pending
+};
+Timer& timer() {
+  static Timer* t = new Timer();  // never destroyed: events may outlive static teardown
+  return *t;
+}
+}  // namespace
+
+void timer_begin(const char* name, hipStream_t stream) {
+  Timer& t = timer();
+  std::lock_guard<std::mutex> lk(t.mu);
+  t.open = -1;
+  if (!t.enabled || t.n >= kTimerSlots) return;
+  const int i = t.n++;
+  t.slot[i].name = name;
+  t.slot[i].used = 1;
+  hipEventRecord(t.start[i], stream);
+  t.open = i;
+}
+
+void timer_end(hipStream_t stream) {
+  Timer& t = timer();
+  std::lock_guard<std::mutex> lk(t.mu);
+  if (t.open >= 0) hipEventRecord(t.stop[t.open], stream);
+  t.open = -1;
+}
+
+}  // namespace fa
+
+using namespace fa;
+
+extern "C" int fa_timer_enable(int enable) {
+  Timer& t = timer();
+  std::lock_guard<std::mutex> lk(t.mu);
+  if (enable && !t.created) {
+    for (int i = 0; i < kTimerSlots; ++i) {
+      if (hipEventCreate(&t.start[i]) != hipSuccess || hipEventCreate(&t.stop[i]) != hipSuccess)
+        return FA_ERR_HIP;
+    }
+    t.created = true;
+  }
+  t.enabled = enable != 0;
+  return FA_OK;
+}
+
+extern "C" void fa_timer_reset(void) {
+  Timer& t = timer();
+  std::lock_guard<std::mutex> lk(t.mu);
+  t.n = 0;
+  t.open = -1;
+}
+
+extern "C" int fa_timer_read(const char* kernel, double* total_ms, int64_t* launches) {
+  if (!kernel || !total_ms || !launches) return FA_ERR_INVALID;
+  Timer& t = timer();
+  std::lock_guard<std::mutex> lk(t.mu);
+  double sum = 0.0;
+  int64_t cnt = 0;
+  for (int i = 0; i < t.n; ++i) {
+    if (strcmp(t.slot[i].name, kernel) != 0) continue;
+    if (hipEventSynchronize(t.stop[i]) != hipSuccess) return FA_ERR_HIP;
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, t.start[i], t.stop[i]) != hipSuccess) return FA_ERR_HIP;
+    sum += ms;
+    ++cnt;
+  }
+  *total_ms = sum;
+  *launches = cnt;
+  return FA_OK;
+}
+
+// ------------------------------------------------------------------------------ checks
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t elem_bytes(int dtype) { return dtype == FA_F32 ? 4 : 2; }
+
+// Shape, dtype and stride checks common to every call.
+int check_desc(const fa_desc* d) {
+  if (!d) return FA_ERR_INVALID;
+  if (d->B < 1 || d->H < 1 || d->N < 1 || d->reserved != 0) return FA_ERR_INVALID;
+  if (d->dtype != FA_BF16 && d->dtype != FA_F32) return FA_ERR_INVALID;
+  if (d->d != 64 && d->d != 128) return FA_ERR_UNSUPPORTED;
+  const int64_t e = (int64_t)elem_bytes(d->dtype);
+  if (d->stride_n < d->d || d->stride_h < 1 || d->stride_b < 1) return FA_ERR_INVALID;
+  if ((d->stride_n * e) % 16 || (d->stride_h * e) % 16 || (d->stride_b * e) % 16) return FA_ERR_INVALID;
+  // grid and index limits of the kernels
+  const int64_t inst = (int64_t)d->B * d->H;
+  if (inst * ((d->N + 127) / 128) > 0x7FFFFFFFll) return FA_ERR_UNSUPPORTED;
+  if (inst * d->N > (int64_t)1 << 40) return FA_ERR_UNSUPPORTED;
+  return FA_OK;
+}
+
+int check_scale(float scale) { return (isfinite(scale) && scale >= 0.f) ? FA_OK : FA_ERR_INVALID; }
+
+int check_ptrs(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (!p || !aligned16(p)) return FA_ERR_INVALID;
+  return FA_OK;
+}
+
+size_t round_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t bwd_ws_bytes(const fa_desc* d) {
+  const size_t rows = (size_t)d->B * d->H * d->N;
+  return round_up(rows * d->d * sizeof(float)) + 2 * round_up(rows * sizeof(float));
+}
+
+size_t lists_bytes(int nb) { return 2 * round_up((size_t)(nb + 1) * 4) + 2 * round_up((size_t)nb * nb * 4); }
+
+int check_block(const fa_desc* d, int32_t bs) {
+  if (bs < 128 || bs % 128 != 0 || d->N % bs != 0) return FA_ERR_INVALID;
+  if (d->N / bs > 1024) return FA_ERR_UNSUPPORTED;
+  return FA_OK;
+}
+
+struct Lists {
+  int32_t *row_ptr, *col_idx, *col_ptr, *row_idx;
+};
+
+Lists carve_lists(void* ws, int nb) {
+  char* p = static_cast<char*>(ws);
+  Lists l;
+  l.row_ptr = reinterpret_cast<int32_t*>(p);
+  p += round_up((size_t)(nb + 1) * 4);
+  l.col_ptr = reinterpret_cast<int32_t*>(p);
+  p += round_up((size_t)(nb + 1) * 4);
+  l.col_idx = reinterpret_cast<int32_t*>(p);
+  p += round_up((size_t)nb * nb * 4);
+  l.row_idx = reinterpret_cast<int32_t*>(p);
+  return l;
+}
+
+void carve_bwd(const fa_desc* d, void* ws, BwdArgs& a) {
+  const size_t rows = (size_t)d->B * d->H * d->N;
+  char* p = static_cast<char*>(ws);
+  a.dq_acc = reinterpret_cast<float*>(p);
+  p += round_up(rows * d->d * sizeof(float));
+  a.delta = reinterpret_cast<float*>(p);
+  p += round_up(rows * sizeof(float));
+  a.lse2 = reinterpret_cast<float*>(p);
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
+
+FwdArgs fwd_args(const fa_desc* d, const void* Q, const void* K, const void* V, float scale, int causal,
+                 const int32_t* key_len, void* O, float* LSE) {
+  FwdArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = Q;
+  a.k = K;
+  a.v = V;
+  a.o = O;
+  a.lse = LSE;
+  a.sb = d->stride_b;
+  a.sh = d->stride_h;
+  a.sn = d->stride_n;
+  a.B = d->B;
+  a.H = d->H;
+  a.N = d->N;
+  a.d = d->d;
+  a.scale = scale;
+  a.causal = causal != 0;
+  a.key_len = key_len;
+  return a;
+}
+
+BwdArgs bwd_args(const fa_desc* d, const void* Q, const void* K, const void* V, const void* O,
+                 const void* dO, const float* LSE, float scale, int causal, const int32_t* key_len,
+                 void* dQ, void* dK, void* dV) {
+  BwdArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = Q;
+  a.k = K;
+  a.v = V;
+  a.o = O;
+  a.dout = dO;
+  a.lse = LSE;
+  a.dq = dQ;
+  a.dk = dK;
+  a.dv = dV;
+  a.sb = d->stride_b;
+  a.sh = d->stride_h;
+  a.sn = d->stride_n;
+  a.B = d->B;
+  a.H = d->H;
+  a.N = d->N;
+  a.d = d->d;
+  a.scale = scale;
+  a.causal = causal != 0;
+  a.key_len = key_len;
+  return a;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------------------ entry points
+
+extern "C" int fa_version(void) { return FA_VERSION; }
+
+extern "C" const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "FA_OK";
+    case FA_ERR_INVALID: return "FA_ERR_INVALID: invalid argument (pointer, shape, stride, alignment or scale)";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: head dim, dtype or size not supported by this call";
+    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing or too small";
+    case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime reported an error";
+    default: return "unknown status";
+  }
+}
+
+extern "C" int fa_fwd(const fa_desc* desc, const void* Q, const void* K, const void* V, float scale,
+                      int causal, const int32_t* key_len, void* O, float* LSE, void* stream) {
+  int st = check_desc(desc);
+  if (st) return st;
+  if ((st = check_scale(scale))) return st;
+  if ((st = check_ptrs({Q, K, V, O, LSE}))) return st;
+  const FwdArgs a = fwd_args(desc, Q, K, V, scale, causal, key_len, O, LSE);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return hip_status(desc->dtype == FA_BF16 ? launch_fwd_bf16(a, s) : launch_fwd_f32(a, s));
+}
+
+extern "C" size_t fa_bwd_workspace_bytes(const fa_desc* desc) {
+  if (check_desc(desc)) return 0;
+  return bwd_ws_bytes(desc);
+}
+
+extern "C" int fa_bwd(const fa_desc* desc, const void* Q, const void* K, const void* V, const void* O,
+                      const void* dO, const float* LSE, float scale, int causal, const int32_t* key_len,
+                      void* dQ, void* dK, void* dV, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_desc(desc);
+  if (st) return st;
+  if (desc->dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if ((st = check_scale(scale))) return st;
+  if ((st = check_ptrs({Q, K, V, O, dO, LSE, dQ, dK, dV}))) return st;
+  if (!workspace || !aligned16(workspace) || workspace_bytes < bwd_ws_bytes(desc)) return FA_ERR_WORKSPACE;
+  BwdArgs a = bwd_args(desc, Q, K, V, O, dO, LSE, scale, causal, key_len, dQ, dK, dV);
+  carve_bwd(desc, workspace, a);
+  return hip_status(launch_bwd_bf16(a, static_cast<hipStream_t>(stream)));
+}
+
+extern "C" size_t fa_blocksparse_workspace_bytes(const fa_desc* desc, int32_t block_size, int backward) {
+  if (check_desc(desc) || check_block(desc, block_size)) return 0;
+  const size_t lists = lists_bytes(desc->N / block_size);
+  return backward ? lists + bwd_ws_bytes(desc) : lists;
+}
+
+extern "C" int fa_blocksparse_fwd(const fa_desc* desc, const void* Q, const void* K, const void* V,
+                                  float scale, const uint8_t* block_mask, int32_t block_size, void* O,
+                                  float* LSE, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_desc(desc);
+  if (st) return st;
+  if (desc->dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if ((st = check_scale(scale))) return st;
+  if ((st = check_ptrs({Q, K, V, O, LSE}))) return st;
+  if (!block_mask) return FA_ERR_INVALID;
+  if ((st = check_block(desc, block_size))) return st;
+  const int nb = desc->N / block_size;
+  if (!workspace || !aligned16(workspace) || workspace_bytes < lists_bytes(nb)) return FA_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Lists l = carve_lists(workspace, nb);
+  hipError_t e = launch_block_lists(block_mask, nb, l.row_ptr, l.col_idx, l.col_ptr, l.row_idx, s);
+  if (e != hipSuccess) return FA_ERR_HIP;
+  FwdArgs a = fwd_args(desc, Q, K, V, scale, 0, nullptr, O, LSE);
+  a.row_ptr = l.row_ptr;
+  a.col_idx = l.col_idx;
+  a.block_size = block_size;
+  return hip_status(launch_fwd_bf16(a, s));
+}
+
+extern "C" int fa_blocksparse_bwd(const fa_desc* desc, const void* Q, const void* K, const void* V,
+                                  const void* O, const void* dO, const float* LSE, float scale,
+                                  const uint8_t* block_mask, int32_t block_size, void* dQ, void* dK,
+                                  void* dV, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_desc(desc);
+  if (st) return st;
+  if (desc->dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if ((st = check_scale(scale))) return st;
+  if ((st = check_ptrs({Q, K, V, O, dO, LSE, dQ, dK, dV}))) return st;
+  if (!block_mask) return FA_ERR_INVALID;
+  if ((st = check_block(desc, block_size))) return st;
+  const int nb = desc->N / block_size;
+  const size_t lb = lists_bytes(nb);
+  if (!workspace || !aligned16(workspace) || workspace_bytes < lb + bwd_ws_bytes(desc)) return FA_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Lists l = carve_lists(workspace, nb);
+  hipError_t e = launch_block_lists(block_mask, nb, l.row_ptr, l.col_idx, l.col_ptr, l.row_idx, s);
+  if (e != hipSuccess) return FA_ERR_HIP;
+  BwdArgs a = bwd_args(desc, Q, K, V, O, dO, LSE, scale, 0, nullptr, dQ, dK, dV);
+  carve_bwd(desc, static_cast<char*>(workspace) + lb, a);
+  a.col_ptr = l.col_ptr;
+  a.row_idx = l.row_idx;
+  a.block_size = block_size;
+  return hip_status(launch_bwd_bf16(a, s));
+}

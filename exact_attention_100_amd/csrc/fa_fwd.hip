@@ -1,0 +1,454 @@
+// Fused exact-attention forward for gfx950.
+//
+// Method: the tiled forward of "FlashAttention: Fast and Memory-Efficient Exact
+// Attention with IO-Awareness" (reading notes (hackmd), §Algorithm › Tiling and
+// Kernel Fusion): a workgroup owns a block of query rows, streams the K/V tiles
+// through on-chip memory, keeps a running row max m and row sum l, rescales its
+// output accumulator whenever m grows, and writes only O and one statistic per
+// row, never the N x N score matrix. The result equals the one-shot softmax
+// exactly (up to rounding) by the incremental-aggregation property the same
+// section states.
+//
+// gfx950 mapping (our design):
+//   * 4 waves x 32 query rows = 128 rows per workgroup; K/V tiles of BC keys,
+//     double-buffered in LDS (K row-major, V transposed so the PV operand is a
+//     pair of 8-byte LDS reads).
+//   * Each wave computes S^T = K Q^T on the 32x32x16 bf16 MFMA, so a lane owns
+//     ONE query column and 16 keys of it: row max / row sum are per-lane
+//     reductions plus one exchange with lane l^32, the rescale factor is one
+//     scalar per lane, and the probabilities already sit in the B-operand layout
+//     of O^T += V^T P^T (no register shuffles).
+//   * Q stays in VGPRs for the whole key loop; O^T accumulates in f32.
+//   * Heaviest causal rows first; all tiles of a head on one XCD.
+#include "fa_common.hpp"
+#include "fa_internal.hpp"
+
+namespace fa {
+
+struct FwdKParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int64_t sb, sh, sn;
+  int B, H, N;
+  float c;  // scale * log2(e): scores are kept in the base-2 domain
+  int causal;
+  const int32_t* key_len;
+  const int32_t* row_ptr;
+  const int32_t* col_idx;
+  int bs;
+  int n_qblocks;
+};
+
+constexpr int kFwdRows = 128;  // query rows per workgroup (4 waves x 32)
+
+// Key range and tile count of one workgroup, shared by the bf16 and f32 kernels.
+struct FwdRange {
+  int kv_len;    // keys >= kv_len are masked for every row of this instance
+  int n_tiles;   // tiles to visit
+  int blk_begin; // sparse: first entry of this query block's list
+};
+
+template <int BC, bool SPARSE>
+__device__ __forceinline__ FwdRange fwd_range(const FwdKParams& p, int b, int q0) {
+  FwdRange r;
+  r.kv_len = p.N;
+  r.blk_begin = 0;
+  if (SPARSE) {
+    const int rb = q0 / p.bs;
+    r.blk_begin = p.row_ptr[rb];
+    r.n_tiles = (p.row_ptr[rb + 1] - r.blk_begin) * (p.bs / BC);
+  } else {
+    if (p.key_len) r.kv_len = min(max(p.key_len[b], 0), p.N);
+    int kv_end = r.kv_len;
+    if (p.causal) kv_end = min(kv_end, q0 + kFwdRows);
+    r.n_tiles = kv_end > 0 ? (kv_end + BC - 1) / BC : 0;
+  }
+  return r;
+}
+
+template <int BC, bool SPARSE>
+__device__ __forceinline__ int fwd_tile_kv0(const FwdKParams& p, const FwdRange& r, int t) {
+  if (SPARSE) {
+    const int tpb = p.bs / BC;
+    const int blk = p.col_idx[r.blk_begin + t / tpb];
+    return blk * p.bs + (t - (t / tpb) * tpb) * BC;
+  }
+  return t * BC;
+}
+
+// One online-softmax step over the S^T registers of a tile (NKB blocks of 32
+// keys; lane = one query, register r of block kb = key kv0 + 32 kb + 8 (r/4) +
+// 4 g + r%4). Masked entries become probability 0. On return s[] holds the
+// unnormalised probabilities 2^(c S - m) and alpha the factor that rescales
+// everything accumulated before this tile.
+template <int NKB>
+__device__ __forceinline__ float online_softmax_step(f32x16 (&s)[NKB], bool need_mask, int kv0,
+                                                     int kv_len, int causal, int qrow, int g,
+                                                     float c, float& m_run, float& l_run) {
+  if (need_mask) {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = kv0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+        const bool ok = key < kv_len && (!causal || key <= qrow);
+        if (!ok) s[kb][r] = kNegInf;
+      }
+  }
+  float mx = kNegInf;
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+  mx = fmaxf(mx, other_half(mx));
+  const float mxs = (mx == kNegInf) ? kNegInf : mx * c;
+  const float m_new = fmaxf(m_run, mxs);
+  const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+  const float alpha = fast_exp2(m_run - m_use);
+  m_run = m_new;
+  float rs = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float pv = fast_exp2(fmaf(s[kb][r], c, -m_use));
+      if (need_mask && s[kb][r] == kNegInf) pv = 0.f;
+      s[kb][r] = pv;
+      rs += pv;
+    }
+  l_run = l_run * alpha + rs;
+  return alpha;
+}
+
+// ----------------------------------------------------------------------------------- bf16
+
+template <int D, int BC, bool SPARSE>
+__global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdKParams p) {
+  constexpr int KP = D + 8;   // K tile row stride (elements): 16-byte rows, banks spread
+  constexpr int VP = BC + 4;  // V^T tile row stride
+  constexpr int NKB = BC / 32;
+  constexpr int NDB = D / 32;
+  constexpr int NKK = D / 16;
+  constexpr int K_CHUNKS = BC * D / 8 / 256;  // 16-byte chunks of K per thread per tile
+  constexpr int V_GROUPS = BC * D / 8 / 256;  // (4 keys x 2 dims) groups of V per thread
+  static_assert(K_CHUNKS >= 1 && V_GROUPS >= 1, "tile too small for 256 threads");
+
+  __shared__ __attribute__((aligned(16))) bf16 sK[2][BC * KP];
+  __shared__ __attribute__((aligned(16))) bf16 sVt[2][D * VP];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, g = lane >> 5;
+  const int N = p.N;
+  int inst, rank;
+  schedule_tile(blockIdx.x, p.B * p.H, p.n_qblocks, inst, rank);
+  const int qb = (!SPARSE && p.causal) ? (p.n_qblocks - 1 - rank) : rank;
+  const int b = inst / p.H, h = inst - b * p.H;
+  const int64_t base = (int64_t)b * p.sb + (int64_t)h * p.sh;
+  const bf16* Qh = static_cast<const bf16*>(p.q) + base;
+  const bf16* Kh = static_cast<const bf16*>(p.k) + base;
+  const bf16* Vh = static_cast<const bf16*>(p.v) + base;
+  const int q0 = qb * kFwdRows;
+  const int qrow = q0 + wave * 32 + l32;
+  const FwdRange rg = fwd_range<BC, SPARSE>(p, b, q0);
+
+  // This lane's query, as the B operand of S^T = K Q^T: slot group g of k-step
+  // kk holds dims [16 kk + 8 g, 16 kk + 8 g + 8).
+  bf16x8 qf[NKK];
+  const u32x4 zero4 = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk)
+    qf[kk] = (qrow < N) ? *reinterpret_cast<const bf16x8*>(Qh + (int64_t)qrow * p.sn + 16 * kk + 8 * g)
+                        : __builtin_bit_cast(bf16x8, zero4);
+
+  u32x4 kreg[K_CHUNKS];
+  uint32_t vreg[V_GROUPS][4];
+  auto load_tile = [&](int kv0) {
+#pragma unroll
+    for (int i = 0; i < K_CHUNKS; ++i) {
+      const int ci = tid + 256 * i, r = ci / (D / 8), cc = ci - r * (D / 8);
+      const int key = kv0 + r;
+      kreg[i] = key < N ? *reinterpret_cast<const u32x4*>(Kh + (int64_t)key * p.sn + 8 * cc) : zero4;
+    }
+#pragma unroll
+    for (int i = 0; i < V_GROUPS; ++i) {
+      const int gi = tid + 256 * i, kq = gi / (D / 2), dc = gi - kq * (D / 2);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int key = kv0 + 4 * kq + j;
+        vreg[i][j] = key < N ? *reinterpret_cast<const uint32_t*>(Vh + (int64_t)key * p.sn + 2 * dc) : 0u;
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < K_CHUNKS; ++i) {
+      const int ci = tid + 256 * i, r = ci / (D / 8), cc = ci - r * (D / 8);
+      *reinterpret_cast<u32x4*>(&sK[buf][r * KP + 8 * cc]) = kreg[i];
+    }
+#pragma unroll
+    for (int i = 0; i < V_GROUPS; ++i) {
+      const int gi = tid + 256 * i, kq = gi / (D / 2), dc = gi - kq * (D / 2);
+      u32x2 xs, ys;
+      split_pairs4(vreg[i][0], vreg[i][1], vreg[i][2], vreg[i][3], xs, ys);
+      *reinterpret_cast<u32x2*>(&sVt[buf][(2 * dc) * VP + 4 * kq]) = xs;
+      *reinterpret_cast<u32x2*>(&sVt[buf][(2 * dc + 1) * VP + 4 * kq]) = ys;
+    }
+  };
+
+  f32x16 oacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+  float m_run = kNegInf, l_run = 0.f;
+
+  if (rg.n_tiles > 0) {
+    load_tile(fwd_tile_kv0<BC, SPARSE>(p, rg, 0));
+    store_tile(0);
+  }
+  __syncthreads();
+
+  for (int t = 0; t < rg.n_tiles; ++t) {
+    const int buf = t & 1;
+    const int kv0 = fwd_tile_kv0<BC, SPARSE>(p, rg, t);
+    if (t + 1 < rg.n_tiles) load_tile(fwd_tile_kv0<BC, SPARSE>(p, rg, t + 1));
+
+    // S^T (keys x queries) = K_tile Q^T
+    f32x16 sacc[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sK[buf][(kb * 32 + l32) * KP + 16 * kk + 8 * g]);
+        sacc[kb] = mfma_bf16(a, qf[kk], sacc[kb]);
+      }
+
+    const bool need_mask =
+        !SPARSE && ((kv0 + BC > rg.kv_len) || (p.causal && kv0 + BC - 1 > q0 + wave * 32));
+    const float alpha = online_softmax_step<NKB>(sacc, need_mask, kv0, rg.kv_len, p.causal, qrow, g,
+                                                 p.c, m_run, l_run);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+
+    // P^T as B operands: k-step ks = 2 kb + s covers keys 32 kb + 16 s + {4g..4g+3, 8+4g..8+4g+3},
+    // which are exactly registers 8 s .. 8 s + 7 of block kb.
+    bf16x8 pb[2 * NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+        pb[2 * kb + s] = pack_bf16x8(sacc[kb][8 * s + 0], sacc[kb][8 * s + 1], sacc[kb][8 * s + 2],
+                                     sacc[kb][8 * s + 3], sacc[kb][8 * s + 4], sacc[kb][8 * s + 5],
+                                     sacc[kb][8 * s + 6], sacc[kb][8 * s + 7]);
+
+    // O^T (dims x queries) += V^T P^T; A = V^T rows (dims) with the same key slots.
+#pragma unroll
+    for (int ks = 0; ks < BC / 16; ++ks)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const bf16* vp = &sVt[buf][(db * 32 + l32) * VP + 16 * ks + 4 * g];
+        const bf16x8 a = concat_bf16x4(*reinterpret_cast<const bf16x4*>(vp),
+                                       *reinterpret_cast<const bf16x4*>(vp + 8));
+        oacc[db] = mfma_bf16(a, pb[ks], oacc[db]);
+      }
+
+    if (t + 1 < rg.n_tiles) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  // Epilogue: O = O_acc / l, LSE = (m + log2 l) ln 2. Rows with no key: O = 0, LSE = -inf.
+  const float l_tot = l_run + other_half(l_run);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (qrow < N) {
+    bf16* Orow = static_cast<bf16*>(p.o) + base + (int64_t)qrow * p.sn;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        u32x2 w;
+        w[0] = pack_bf16x2(oacc[db][4 * j + 0] * inv, oacc[db][4 * j + 1] * inv);
+        w[1] = pack_bf16x2(oacc[db][4 * j + 2] * inv, oacc[db][4 * j + 3] * inv);
+        *reinterpret_cast<u32x2*>(Orow + db * 32 + 8 * j + 4 * g) = w;
+      }
+    if (g == 0)
+      p.lse[(int64_t)inst * N + qrow] = l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : kNegInf;
+  }
+}
+
+// ------------------------------------------------------------------------------------ f32
+
+// Same schedule and softmax; products on the 32x32x2 f32 MFMA (K index = lane group),
+// so both K and V stay row-major in LDS.
+template <int D>
+__global__ __launch_bounds__(256) void fwd_f32_kernel(FwdKParams p) {
+  constexpr int BC = 32;
+  constexpr int KP = D + 4;  // 16-byte rows
+  constexpr int VP = D + 8;  // lane groups (keys 4 apart) land on different banks
+  constexpr int NDB = D / 32;
+  constexpr int CHUNKS = BC * D / 4 / 256;  // 16-byte chunks per thread per tile (K and V each)
+  static_assert(CHUNKS >= 1, "tile too small");
+
+  __shared__ __attribute__((aligned(16))) float sK[2][BC * KP];
+  __shared__ __attribute__((aligned(16))) float sV[2][BC * VP];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, g = lane >> 5;
+  const int N = p.N;
+  int inst, rank;
+  schedule_tile(blockIdx.x, p.B * p.H, p.n_qblocks, inst, rank);
+  const int qb = p.causal ? (p.n_qblocks - 1 - rank) : rank;
+  const int b = inst / p.H, h = inst - b * p.H;
+  const int64_t base = (int64_t)b * p.sb + (int64_t)h * p.sh;
+  const float* Qh = static_cast<const float*>(p.q) + base;
+  const float* Kh = static_cast<const float*>(p.k) + base;
+  const float* Vh = static_cast<const float*>(p.v) + base;
+  const int q0 = qb * kFwdRows;
+  const int qrow = q0 + wave * 32 + l32;
+  const FwdRange rg = fwd_range<BC, false>(p, b, q0);
+
+  float qf[D / 2];  // k-step kk: dim 2 kk + g
+#pragma unroll
+  for (int kk = 0; kk < D / 2; ++kk) qf[kk] = (qrow < N) ? Qh[(int64_t)qrow * p.sn + 2 * kk + g] : 0.f;
+
+  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+  f32x4 kreg[CHUNKS], vreg[CHUNKS];
+  auto load_tile = [&](int kv0) {
+#pragma unroll
+    for (int i = 0; i < CHUNKS; ++i) {
+      const int ci = tid + 256 * i, r = ci / (D / 4), cc = ci - r * (D / 4);
+      const int key = kv0 + r;
+      kreg[i] = key < N ? *reinterpret_cast<const f32x4*>(Kh + (int64_t)key * p.sn + 4 * cc) : zero4;
+      vreg[i] = key < N ? *reinterpret_cast<const f32x4*>(Vh + (int64_t)key * p.sn + 4 * cc) : zero4;
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < CHUNKS; ++i) {
+      const int ci = tid + 256 * i, r = ci / (D / 4), cc = ci - r * (D / 4);
+      *reinterpret_cast<f32x4*>(&sK[buf][r * KP + 4 * cc]) = kreg[i];
+      *reinterpret_cast<f32x4*>(&sV[buf][r * VP + 4 * cc]) = vreg[i];
+    }
+  };
+
+  f32x16 oacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+  float m_run = kNegInf, l_run = 0.f;
+
+  if (rg.n_tiles > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  __syncthreads();
+
+  for (int t = 0; t < rg.n_tiles; ++t) {
+    const int buf = t & 1;
+    const int kv0 = t * BC;
+    if (t + 1 < rg.n_tiles) load_tile(kv0 + BC);
+
+    f32x16 sacc[1];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sacc[0][r] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < D / 2; ++kk) sacc[0] = mfma_f32(sK[buf][l32 * KP + 2 * kk + g], qf[kk], sacc[0]);
+
+    const bool need_mask = (kv0 + BC > rg.kv_len) || (p.causal && kv0 + BC - 1 > q0 + wave * 32);
+    const float alpha = online_softmax_step<1>(sacc, need_mask, kv0, rg.kv_len, p.causal, qrow, g, p.c,
+                                               m_run, l_run);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+
+    // O^T += V^T P^T: k-step r uses key 8 (r/4) + 4 g + r%4 in lane group g.
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = 8 * (r >> 2) + 4 * g + (r & 3);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+        oacc[db] = mfma_f32(sV[buf][key * VP + db * 32 + l32], sacc[0][r], oacc[db]);
+    }
+
+    if (t + 1 < rg.n_tiles) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  const float l_tot = l_run + other_half(l_run);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (qrow < N) {
+    float* Orow = static_cast<float*>(p.o) + base + (int64_t)qrow * p.sn;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        f32x4 w;
+        w[0] = oacc[db][4 * j + 0] * inv;
+        w[1] = oacc[db][4 * j + 1] * inv;
+        w[2] = oacc[db][4 * j + 2] * inv;
+        w[3] = oacc[db][4 * j + 3] * inv;
+        *reinterpret_cast<f32x4*>(Orow + db * 32 + 8 * j + 4 * g) = w;
+      }
+    if (g == 0)
+      p.lse[(int64_t)inst * N + qrow] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : kNegInf;
+  }
+}
+
+// ------------------------------------------------------------------------------ launchers
+
+static FwdKParams make_params(const FwdArgs& a) {
+  FwdKParams p;
+  p.q = a.q;
+  p.k = a.k;
+  p.v = a.v;
+  p.o = a.o;
+  p.lse = a.lse;
+  p.sb = a.sb;
+  p.sh = a.sh;
+  p.sn = a.sn;
+  p.B = a.B;
+  p.H = a.H;
+  p.N = a.N;
+  p.c = a.scale * kLog2e;
+  p.causal = a.causal;
+  p.key_len = a.key_len;
+  p.row_ptr = a.row_ptr;
+  p.col_idx = a.col_idx;
+  p.bs = a.block_size;
+  p.n_qblocks = (a.N + kFwdRows - 1) / kFwdRows;
+  return p;
+}
+
+hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s) {
+  const FwdKParams p = make_params(a);
+  const dim3 grid((unsigned)(a.B * a.H * p.n_qblocks)), block(256);
+  const bool sparse = a.row_ptr != nullptr;
+  timer_begin("fa_fwd_bf16", s);
+  if (a.d == 128) {
+    if (sparse) fwd_bf16_kernel<128, 64, true><<<grid, block, 0, s>>>(p);
+    else fwd_bf16_kernel<128, 64, false><<<grid, block, 0, s>>>(p);
+  } else {
+    if (sparse) fwd_bf16_kernel<64, 64, true><<<grid, block, 0, s>>>(p);
+    else fwd_bf16_kernel<64, 64, false><<<grid, block, 0, s>>>(p);
+  }
+  timer_end(s);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s) {
+  const FwdKParams p = make_params(a);
+  const dim3 grid((unsigned)(a.B * a.H * p.n_qblocks)), block(256);
+  timer_begin("fa_fwd_f32", s);
+  if (a.d == 128) fwd_f32_kernel<128><<<grid, block, 0, s>>>(p);
+  else fwd_f32_kernel<64><<<grid, block, 0, s>>>(p);
+  timer_end(s);
+  return hipGetLastError();
+}
+
+}  // namespace fa

@@ -1,0 +1,63 @@
+// Host-side interface between the C ABI (fa_api.hip) and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+// Everything a forward launch needs. Pointers are device pointers.
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int64_t sb, sh, sn;  // element strides shared by q, k, v, o
+  int B, H, N, d;
+  float scale;
+  int causal;
+  const int32_t* key_len;  // device [B] or nullptr
+  // Block-sparse (row_ptr != nullptr): CSR lists of kept key blocks per query block.
+  const int32_t* row_ptr;
+  const int32_t* col_idx;
+  int block_size;
+};
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  int64_t sb, sh, sn;
+  int B, H, N, d;
+  float scale;
+  int causal;
+  const int32_t* key_len;
+  // workspace sections
+  float* dq_acc;  // [B, H, N, d] float32
+  float* delta;   // [B, H, N]: rowsum(dO o O)
+  float* lse2;    // [B, H, N]: LSE * log2(e) (+inf for rows with no key)
+  // Block-sparse (col_ptr != nullptr): CSC lists of kept query blocks per key block.
+  const int32_t* col_ptr;
+  const int32_t* row_idx;
+  int block_size;
+};
+
+// Kernel timer hooks (fa_api.hip): bracket one launch with events.
+void timer_begin(const char* name, hipStream_t stream);
+void timer_end(hipStream_t stream);
+
+hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s);
+hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s);
+hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s);
+// Builds row_ptr[nb+1], col_idx[nb*nb], col_ptr[nb+1], row_idx[nb*nb] from the mask.
+hipError_t launch_block_lists(const uint8_t* mask, int nb, int32_t* row_ptr, int32_t* col_idx,
+                              int32_t* col_ptr, int32_t* row_idx, hipStream_t s);
+
+}  // namespace fa

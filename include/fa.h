@@ -1,0 +1,143 @@
+/*
+ * fa.h -- C ABI of the MI355X (gfx950) exact-attention library (libfa.so).
+ *
+ * The library computes exact attention O = softmax(scale * Q K^T) V with the
+ * tiled, IO-aware method: one fused forward kernel that never writes the N x N
+ * score matrix to HBM and saves only O and one log-sum-exp per row, and a
+ * backward that recomputes the probabilities block by block from that
+ * statistic ("FlashAttention: Fast and Memory-Efficient Exact Attention with
+ * IO-Awareness", reading notes (hackmd): §Background › Standard Attention
+ * Implementation for S, P and O; §Algorithm › Tiling, Recomputation and Kernel
+ * Fusion for the method; §Introduction › Block-sparse FlashAttention for the
+ * block-sparse variant).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Tensors.  Q, K, V, O, dO, dQ, dK, dV are [B, H, N, d] arrays of the
+ *   descriptor's dtype whose last dimension is contiguous; element (b, h, n, i)
+ *   lives at base + b*stride_b + h*stride_h + n*stride_n + i (strides in
+ *   elements, shared by all of them). Queries and keys have the same length N.
+ *   LSE is a contiguous float32 [B, H, N] array.
+ * Pointers.  Every tensor, key_len, block_mask and workspace pointer is a
+ *   DEVICE pointer owned by the caller; the library never allocates or frees
+ *   device memory. Base pointers must be 16-byte aligned, and stride_n * (bytes
+ *   per element) a multiple of 16. Outputs must not alias inputs.
+ * Streams.  `stream` is a hipStream_t (NULL = the default stream). Work is
+ *   enqueued on it and the call returns without synchronising: inputs must stay
+ *   alive, and outputs must not be read, until the stream reaches that point.
+ * Masking.  Entry (i, j) of S is kept iff every active mask keeps it; masked
+ *   entries are -inf before the softmax, so they get probability 0:
+ *     causal != 0   keeps key j for query i iff j <= i;
+ *     key_len       (device int32 [B], or NULL) keeps key j iff j < key_len[b]
+ *                   (values are clamped to [0, N] on the device);
+ *     block_mask    (block-sparse calls) keeps (i, j) iff
+ *                   block_mask[(i / bs) * (N / bs) + j / bs] != 0.
+ *   A query row with no kept key gets O = 0, LSE = -inf and no gradient.
+ * Numbers.  All products accumulate in float32. bf16 outputs are rounded to
+ *   nearest even. LSE[i] = m_i + ln(l_i), natural log, where m_i is the row
+ *   max of the scaled, masked S and l_i the row sum of exp(S - m_i).
+ *   `scale` must be finite and >= 0. Inputs must be finite.
+ * Errors.  Every call returns FA_OK (0) or a negative FA_ERR_* code. Argument
+ *   checks run before anything is enqueued; a failed check enqueues nothing.
+ *   FA_ERR_HIP reports a launch error from the HIP runtime.
+ * Threads.  Calls are reentrant; they share no state except the optional
+ *   kernel timer below.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FA_VERSION 100
+
+enum fa_status {
+  FA_OK = 0,
+  FA_ERR_INVALID = -1,     /* null pointer, bad shape, stride, alignment or scale */
+  FA_ERR_UNSUPPORTED = -2, /* d not in {64, 128}, or dtype not built for this call */
+  FA_ERR_WORKSPACE = -3,   /* workspace pointer null or smaller than required */
+  FA_ERR_HIP = -4          /* the HIP runtime reported an error at launch */
+};
+
+enum fa_dtype { FA_BF16 = 0, FA_F32 = 1 };
+
+typedef struct fa_desc {
+  int32_t B, H, N, d; /* batch, heads, sequence length (>= 1), head dim (64 or 128) */
+  int32_t dtype;      /* FA_BF16 or FA_F32 */
+  int32_t reserved;   /* must be 0 */
+  int64_t stride_b, stride_h, stride_n; /* element strides; the d stride is 1 */
+} fa_desc;
+
+/* Forward: O = softmax(scale * Q K^T + mask) V and LSE (see above).
+ * Reads Q, K, V (and key_len); writes O and LSE. bf16 and fp32.
+ * Defines: S = QK^T, P = softmax(S), O = PV (reading notes, §Background ›
+ * Standard Attention Implementation), computed tile by tile with the running
+ * row max and row sum of §Algorithm › Tiling; only O, m and l leave the chip
+ * (§Recomputation), stored here as LSE = m + ln l. */
+int fa_fwd(const fa_desc* desc, const void* Q, const void* K, const void* V, float scale,
+           int causal, const int32_t* key_len, void* O, float* LSE, void* stream);
+
+/* Bytes of device workspace fa_bwd needs: a float32 dQ accumulator and one
+ * float32 per row, i.e. O(N d) per head and never O(N^2) (the linear extra
+ * memory of Theorem 1, anthology LIT-074 key takeaways). */
+size_t fa_bwd_workspace_bytes(const fa_desc* desc);
+
+/* Backward: the gradient of <dO, O> with respect to Q, K and V, given the O and
+ * LSE that fa_fwd produced for the same Q, K, V, scale, causal and key_len.
+ * Recomputes P = exp(scale * Q K^T - LSE) tile by tile (reading notes,
+ * §Algorithm › Recomputation), then dV = P^T dO, dP = dO V^T,
+ * dS = P o (dP - rowsum(dO o O)), dQ = scale dS K, dK = scale dS^T Q.
+ * Keys that no query may see get dK = dV = 0. bf16 only (fp32:
+ * FA_ERR_UNSUPPORTED). `workspace` must hold fa_bwd_workspace_bytes(desc)
+ * bytes; its contents on entry are ignored. */
+int fa_bwd(const fa_desc* desc, const void* Q, const void* K, const void* V, const void* O,
+           const void* dO, const float* LSE, float scale, int causal, const int32_t* key_len,
+           void* dQ, void* dK, void* dV, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace the block-sparse calls need for block_size `bs`
+ * (the per-row and per-column lists of kept blocks; the backward adds the
+ * fa_bwd workspace). Returns 0 for an invalid descriptor or block size. */
+size_t fa_blocksparse_workspace_bytes(const fa_desc* desc, int32_t block_size, int backward);
+
+/* Block-sparse forward: fa_fwd restricted to the nonzero blocks of
+ * `block_mask` (device uint8 [N/bs][N/bs], row = query block, shared over B
+ * and H); zero blocks are never loaded or computed (reading notes,
+ * §Introduction › Block-sparse FlashAttention). Requires N % bs == 0 and bs a
+ * positive multiple of 128. No causal or key_len. bf16 only. */
+int fa_blocksparse_fwd(const fa_desc* desc, const void* Q, const void* K, const void* V,
+                       float scale, const uint8_t* block_mask, int32_t block_size, void* O,
+                       float* LSE, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Block-sparse backward: fa_bwd restricted to the nonzero blocks; needs the O
+ * and LSE of fa_blocksparse_fwd with the same mask. Same requirements. */
+int fa_blocksparse_bwd(const fa_desc* desc, const void* Q, const void* K, const void* V,
+                       const void* O, const void* dO, const float* LSE, float scale,
+                       const uint8_t* block_mask, int32_t block_size, void* dQ, void* dK,
+                       void* dV, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static, human-readable name of a status code. */
+const char* fa_status_string(int status);
+
+/* FA_VERSION of the built library. */
+int fa_version(void);
+
+/* Optional kernel timer (instrumentation for benchmarks). When enabled, every
+ * kernel the library launches is bracketed by two HIP events on its stream.
+ * fa_timer_read synchronises on the recorded events and returns the summed
+ * duration (ms) and launch count of the kernels whose name equals `kernel`
+ * since the last reset. Process-wide state; not for concurrent use. Up to 8192
+ * launches are recorded between resets; later ones are not timed.
+ * fa_timer_enable returns FA_OK or FA_ERR_HIP (events could not be created). */
+int fa_timer_enable(int enable);
+void fa_timer_reset(void);
+int fa_timer_read(const char* kernel, double* total_ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

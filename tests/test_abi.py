@@ -1,0 +1,94 @@
+"""CPU checks of the C ABI: the library loads, exports every symbol the header
+declares, and rejects bad arguments before touching the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from helpers import ROOT, ensure_library
+
+
+@pytest.fixture(scope="module")
+def lib():
+    ensure_library()
+    import exact_attention_100_amd as fa
+    return fa.lib()
+
+
+def _header_functions():
+    with open(os.path.join(ROOT, "include", "fa.h")) as fh:
+        text = fh.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_expected_entry_points():
+    names = _header_functions()
+    for n in ("fa_fwd", "fa_bwd", "fa_blocksparse_fwd", "fa_blocksparse_bwd", "fa_bwd_workspace_bytes",
+              "fa_blocksparse_workspace_bytes", "fa_status_string", "fa_version"):
+        assert n in names
+
+
+def test_library_exports_every_header_symbol(lib):
+    cdll = ctypes.CDLL(os.path.join(ROOT, "exact_attention_100_amd", "lib", "libfa.so"))
+    for n in _header_functions():
+        assert hasattr(cdll, n), n
+
+
+def test_version_and_status_strings(lib):
+    assert lib.fa_version() == 100
+    for code in (0, -1, -2, -3, -4):
+        assert lib.fa_status_string(code)
+    assert b"unknown" in lib.fa_status_string(7)
+
+
+def _desc(B=2, H=3, N=256, d=64, dtype=0):
+    from exact_attention_100_amd import FaDesc
+    return FaDesc(B, H, N, d, dtype, 0, H * N * d, N * d, d)
+
+
+A = 4096  # a 16-byte aligned, never dereferenced address
+
+
+def test_argument_errors_before_any_launch(lib):
+    d = _desc()
+    ref = ctypes.byref
+    assert lib.fa_fwd(ref(d), None, A, A, 0.1, 0, None, A, A, None) == -1
+    assert lib.fa_fwd(ref(d), A + 2, A, A, 0.1, 0, None, A, A, None) == -1  # misaligned
+    assert lib.fa_fwd(ref(d), A, A, A, -0.5, 0, None, A, A, None) == -1
+    assert lib.fa_fwd(ref(d), A, A, A, float("nan"), 0, None, A, A, None) == -1
+    assert lib.fa_fwd(None, A, A, A, 0.1, 0, None, A, A, None) == -1
+    for bad in (_desc(N=0), _desc(B=0), _desc(dtype=5)):
+        assert lib.fa_fwd(ref(bad), A, A, A, 0.1, 0, None, A, A, None) == -1
+    assert lib.fa_fwd(ref(_desc(d=96)), A, A, A, 0.1, 0, None, A, A, None) == -2
+    odd = _desc()
+    odd.stride_n = 65  # row stride not a multiple of 16 bytes
+    assert lib.fa_fwd(ref(odd), A, A, A, 0.1, 0, None, A, A, None) == -1
+    # backward: fp32 unsupported, workspace checks
+    assert lib.fa_bwd(ref(_desc(dtype=1)), A, A, A, A, A, A, 0.1, 0, None, A, A, A, A, 1 << 30, None) == -2
+    need = lib.fa_bwd_workspace_bytes(ref(d))
+    assert lib.fa_bwd(ref(d), A, A, A, A, A, A, 0.1, 0, None, A, A, A, A, need - 1, None) == -3
+    assert lib.fa_bwd(ref(d), A, A, A, A, A, A, 0.1, 0, None, A, A, A, None, need, None) == -3
+    # block-sparse: block size must be a multiple of 128 that divides N
+    for bs in (64, 100, 192, 512):
+        assert lib.fa_blocksparse_fwd(ref(d), A, A, A, 0.1, A, bs, A, A, A, 1 << 30, None) == -1
+    assert lib.fa_blocksparse_fwd(ref(d), A, A, A, 0.1, None, 128, A, A, A, 1 << 30, None) == -1
+    assert lib.fa_blocksparse_fwd(ref(d), A, A, A, 0.1, A, 128, A, A, A, 16, None) == -3
+    assert lib.fa_blocksparse_workspace_bytes(ref(d), 100, 0) == 0
+
+
+def test_workspace_is_linear_in_sequence_length(lib):
+    """Extra memory grows as O(N) (Theorem 1), never O(N^2)."""
+    ws = [lib.fa_bwd_workspace_bytes(ctypes.byref(_desc(B=1, H=1, N=n, d=128))) for n in (4096, 8192, 16384)]
+    per_row = [w / n for w, n in zip(ws, (4096, 8192, 16384))]
+    assert max(per_row) - min(per_row) < 1.0
+    assert per_row[0] <= (128 + 2) * 4 + 1
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    from exact_attention_100_amd import _lib
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(_lib, "_LIB", None)
+    with pytest.raises(FileNotFoundError):
+        _lib.lib()

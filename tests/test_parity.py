@@ -1,0 +1,223 @@
+"""Parity of the HIP path (through the C ABI) with the float64 oracle, on the GPU.
+
+Every case prints its name, seed and shape before touching the GPU.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import workloads
+from helpers import (TOL_O_BF16, compare, ensure_library, run_gpu, run_oracle, upload)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    ensure_library()
+    yield
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+def _check_case(case, heads=None, backward=True):
+    _say(case.name, "seed", case.seed, "B,H,N,d", case.B, case.H, case.N, case.d, case.dtype,
+         "causal" if case.causal else "", "key_len" if case.key_len is not None else "",
+         "block" if case.block_mask is not None else "", "heads", heads)
+    gpu = run_gpu(case, backward=backward)
+    ref = run_oracle(case, backward=backward, heads=heads)
+    errs = compare(gpu, ref, case, heads=heads, backward=backward)
+    _say("errors", errs)
+    return gpu, ref
+
+
+# ----------------------------------------------------------------------------- named workloads
+
+def test_c1_fp32_forward():
+    _check_case(workloads.make_config("C1"), backward=False)
+
+
+@pytest.mark.parametrize("name", ["C2", "C3"])
+def test_full_config_all_heads(name):
+    _check_case(workloads.make_config(name))
+
+
+@pytest.mark.parametrize("name,heads", [("C4a", [(0, 0), (1, 9)]), ("C4b", [(0, 3), (1, 15)]),
+                                        ("C5", [(0, 0), (0, 5)])])
+def test_full_config_sampled_heads(name, heads):
+    _check_case(workloads.make_config(name), heads=heads)
+
+
+@pytest.mark.parametrize("name", ["C2", "C3"])
+def test_extra_seeds(name):
+    _check_case(workloads.make_config(name, seed=101 + int(name[1])))
+
+
+# ----------------------------------------------------------------------------- edge cases
+
+@pytest.mark.parametrize("N", [1, 2, 4, 31, 127, 129, 200])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("mask", ["none", "causal", "key_len"])
+def test_ragged_sizes_bf16(N, d, mask):
+    case = workloads.make_case(2, 2, N, d, mask=mask, seed=1000 + N + d, key_len_range=(0, N),
+                               name=f"ragged-{mask}")
+    _check_case(case)
+
+
+@pytest.mark.parametrize("N", [1, 33, 128, 300])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("mask", ["none", "causal", "key_len"])
+def test_fp32_forward_sizes(N, d, mask):
+    case = workloads.make_case(2, 3, N, d, dtype=workloads.F32, mask=mask, seed=2000 + N + d,
+                               key_len_range=(1, N), name=f"fp32-{mask}")
+    _check_case(case, backward=False)
+
+
+def test_key_len_zero_rows_have_no_keys():
+    case = workloads.make_case(3, 2, 150, 64, mask="key_len", seed=7, name="key_len-0")
+    case.key_len = np.array([0, 150, 1], dtype=np.int32)
+    gpu, _ = _check_case(case)
+    assert np.all(gpu["o"][0] == 0) and np.all(np.isneginf(gpu["lse"][0]))
+    assert np.all(gpu["dq"][0] == 0) and np.all(gpu["dk"][0] == 0) and np.all(gpu["dv"][0] == 0)
+    assert np.all(gpu["dk"][2, :, 1:] == 0) and np.all(gpu["dv"][2, :, 1:] == 0)
+
+
+def test_hand_case_n4_padded_to_d64():
+    """q_i = e_0, k_j = j e_0, scale ln 2: weights 2^j. Values are bf16-exact."""
+    case = workloads.make_case(1, 1, 4, 64, mask="causal", seed=0, scale=math.log(2.0), name="hand-n4")
+    q = np.zeros((1, 1, 4, 64), np.float32)
+    q[..., 0] = 1
+    k = np.zeros_like(q)
+    k[0, 0, :, 0] = np.arange(4)
+    v = np.zeros_like(q)
+    v[0, 0, :, :2] = [[1, 0], [0, 1], [1, 1], [0, 0]]
+    case.q, case.k, case.v = q, k, v
+    gpu, _ = _check_case(case)
+    # the causal hand values, up to bf16 rounding of O
+    exp = np.array([[1, 0], [1 / 3, 2 / 3], [5 / 7, 6 / 7], [1 / 3, 2 / 5]])
+    assert np.max(np.abs(gpu["o"][0, 0, :, :2] - exp)) < 4e-3
+    assert np.all(gpu["o"][0, 0, :, 2:] == 0)
+
+
+def test_scale_zero_is_mean_of_values():
+    case = workloads.make_case(1, 2, 96, 64, mask="causal", seed=11, scale=0.0, name="scale-0")
+    gpu, _ = _check_case(case)
+    cum = np.cumsum(case.v[0].astype(np.float64), axis=1) / np.arange(1, 97)[None, :, None]
+    assert np.max(np.abs(gpu["o"][0] - cum)) <= TOL_O_BF16
+
+
+def test_monotone_logits_rescale_every_tile():
+    """Scores grow along the keys so the running max changes on every tile."""
+    N, d = 512, 128
+    case = workloads.make_case(1, 2, N, d, seed=12, name="monotone")
+    rng = np.random.default_rng(12)
+    q = np.zeros((1, 2, N, d), np.float32)
+    q[..., 0] = 1.0
+    k = workloads.bf16_round((rng.standard_normal((1, 2, N, d)) * 0.1).astype(np.float32))
+    k[..., 0] = workloads.bf16_round(np.linspace(-8, 8, N, dtype=np.float32))
+    case.q, case.k = workloads.bf16_round(q), k
+    case.scale = np.float32(1.0)
+    _check_case(case)
+
+
+def test_large_logits():
+    case = workloads.make_case(2, 2, 300, 64, mask="causal", seed=13, scale=1.0, name="large-logits")
+    _check_case(case)
+
+
+def test_strided_bnhd_layout_matches_contiguous():
+    import torch
+    import exact_attention_100_amd as fa
+    case = workloads.make_case(2, 3, 200, 64, mask="causal", seed=14, name="strided")
+    _say(case.name)
+    t = upload(case)
+    # same values in a [B, N, H, d] buffer viewed as [B, H, N, d]
+    s = {n: t[n].permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3) for n in ("q", "k", "v", "do")}
+    o1, l1 = fa.fwd(t["q"], t["k"], t["v"], causal=True)
+    o2, l2 = fa.fwd(s["q"], s["k"], s["v"], causal=True)
+    g1 = fa.bwd(t["q"], t["k"], t["v"], o1, t["do"], l1, causal=True)
+    g2 = fa.bwd(s["q"], s["k"], s["v"], o2, s["do"], l2, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    for a, b in zip(g1[1:], g2[1:]):
+        assert torch.equal(a, b)
+    assert torch.allclose(g1[0].float(), g2[0].float(), atol=1e-2, rtol=0)
+
+
+def test_deterministic_outputs():
+    import torch
+    import exact_attention_100_amd as fa
+    case = workloads.make_case(2, 4, 700, 128, mask="causal", seed=15, name="determinism")
+    _say(case.name)
+    t = upload(case)
+    o1, l1 = fa.fwd(t["q"], t["k"], t["v"], causal=True)
+    o2, l2 = fa.fwd(t["q"], t["k"], t["v"], causal=True)
+    _, dk1, dv1 = fa.bwd(t["q"], t["k"], t["v"], o1, t["do"], l1, causal=True)
+    _, dk2, dv2 = fa.bwd(t["q"], t["k"], t["v"], o1, t["do"], l1, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert torch.equal(dk1, dk2) and torch.equal(dv1, dv2)
+
+
+# ----------------------------------------------------------------------------- block-sparse
+
+@pytest.mark.parametrize("kind", ["ones", "diag", "random", "empty-row"])
+@pytest.mark.parametrize("d,bs", [(64, 128), (128, 128), (64, 256)])
+def test_block_sparse_masks(kind, d, bs):
+    N = 4 * bs
+    case = workloads.make_case(1, 3, N, d, mask="block", block_size=bs, seed=16, name=f"block-{kind}")
+    nb = N // bs
+    if kind == "ones":
+        case.block_mask = np.ones((nb, nb), np.uint8)
+    elif kind == "diag":
+        case.block_mask = np.eye(nb, dtype=np.uint8)
+    elif kind == "random":
+        case.block_mask = (np.random.default_rng(3).random((nb, nb)) < 0.4).astype(np.uint8)
+        case.block_mask[0, 3] = 1
+    else:
+        m = np.ones((nb, nb), np.uint8)
+        m[1, :] = 0  # query block 1 has no key: O = 0, LSE = -inf
+        m[:, 2] = 0  # key block 2 is seen by nobody: dK = dV = 0
+        case.block_mask = m
+    gpu, _ = _check_case(case)
+    if kind == "empty-row":
+        assert np.all(gpu["o"][:, :, bs:2 * bs] == 0) and np.all(np.isneginf(gpu["lse"][:, :, bs:2 * bs]))
+        assert np.all(gpu["dk"][:, :, 2 * bs:3 * bs] == 0) and np.all(gpu["dv"][:, :, 2 * bs:3 * bs] == 0)
+
+
+def test_block_sparse_all_ones_equals_dense_kernel():
+    import torch
+    import exact_attention_100_amd as fa
+    case = workloads.make_case(1, 2, 512, 128, seed=17, name="sparse-vs-dense")
+    _say(case.name)
+    t = upload(case)
+    ones = torch.ones((4, 4), dtype=torch.uint8, device="cuda")
+    o1, l1 = fa.fwd(t["q"], t["k"], t["v"])
+    o2, l2 = fa.blocksparse_fwd(t["q"], t["k"], t["v"], ones, 128)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+# ----------------------------------------------------------------------------- error paths
+
+def test_errors_raise_through_binding():
+    import torch
+    import exact_attention_100_amd as fa
+    x = torch.zeros((1, 1, 64, 64), dtype=torch.float32, device="cuda")
+    o, lse = fa.fwd(x, x, x)
+    with pytest.raises(fa.FAError) as ei:
+        fa.bwd(x, x, x, o, x, lse)
+    assert ei.value.status == -2
+    y = torch.zeros((1, 1, 64, 96), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(fa.FAError) as ei:
+        fa.fwd(y, y, y)
+    assert ei.value.status == -2
+    z = torch.zeros((1, 1, 64, 64), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(fa.FAError) as ei:
+        fa.fwd(z, z, z, scale=-1.0)
+    assert ei.value.status == -1
