@@ -1,0 +1,217 @@
+"""Benchmark: exact attention forward + backward on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload C4b]
+
+One step = one fa_fwd + one fa_bwd (every kernel of the hot path) over one batch
+of seeded synthetic bf16 inputs already resident in HBM. Prints one JSON line.
+
+value    = whole-job algorithmic TFLOP/s = 14 d (kept query/key pairs) / step time
+           (forward 4 d per pair: Q K^T and P V; backward 10 d: the Q K^T recompute,
+           P^T dO, dO V^T, dS^T Q and dS K).
+roofline = the dominant kernel's algorithmic FLOP per launch / its mean launch time,
+           timed with HIP events on its own stream, against the bf16 MFMA peak.
+cpu_baseline = the float64 CPU oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk/CU
+KERNEL_SOURCES = ["exact_attention_100_amd/csrc/fa_fwd.hip", "exact_attention_100_amd/csrc/fa_bwd.hip",
+                  "exact_attention_100_amd/csrc/fa_common.hpp"]
+
+
+def kept_pairs(case) -> int:
+    """Number of (query, key) pairs the masks keep, summed over all instances."""
+    import numpy as np
+    B, H, N = case.B, case.H, case.N
+    if case.block_mask is not None:
+        return int(case.block_mask.astype(np.int64).sum()) * case.block_size ** 2 * B * H
+    per_b = []
+    for b in range(B):
+        L = N if case.key_len is None else int(min(max(case.key_len[b], 0), N))
+        if case.causal:
+            # sum over rows i of min(i + 1, L)
+            i = np.arange(N, dtype=np.int64)
+            per_b.append(int(np.minimum(i + 1, L).sum()))
+        else:
+            per_b.append(N * L)
+    return int(sum(per_b)) * H
+
+
+def sources_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel: str, workload: str):
+    """HBM bytes per launch measured by rocprofv3 counters, if taken on the current sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("sources_hash") != sources_hash():
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(case, budget_s: float):
+    """Time the float64 oracle (fwd + bwd) on whole heads of the workload until the budget is used."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    heads = [(b, h) for b in range(case.B) for h in range(case.H)]
+    done = []
+    t0 = time.perf_counter()
+    for bh in heads:
+        oracle.forward(case.q, case.k, case.v, float(case.scale), causal=case.causal, key_len=case.key_len,
+                       block_mask=case.block_mask, block_size=case.block_size, heads=[bh])
+        oracle.backward(case.q, case.k, case.v, case.do, float(case.scale), causal=case.causal,
+                        key_len=case.key_len, block_mask=case.block_mask, block_size=case.block_size,
+                        heads=[bh])
+        done.append(bh)
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    el = time.perf_counter() - t0
+    flops = 14 * case.d * kept_pairs(case) * len(done) / (case.B * case.H)
+    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"float64 fwd+bwd of {len(done)} of {case.B * case.H} (batch, head) instances "
+                      f"at full N={case.N}, d={case.d}; {el:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="C4b")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not supported",
+              file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import exact_attention_100_amd as fa
+    import workloads
+    from exact_attention_100_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from exact_attention_100_amd.build import build
+        build()
+
+    case = workloads.make_config(args.workload)
+    assert case.dtype == workloads.BF16, "the bench measures bf16 workloads"
+    dev = torch.device("cuda:0")
+    t = {n: torch.from_numpy(case.bits(n).view(np.int16)).view(torch.bfloat16).to(dev)
+         for n in ("q", "k", "v", "do")}
+    key_len = None if case.key_len is None else torch.from_numpy(case.key_len).to(dev)
+    bmask = None if case.block_mask is None else torch.from_numpy(case.block_mask).to(dev)
+    sc = float(case.scale)
+    o = torch.empty_like(t["q"])
+    lse = torch.empty((case.B, case.H, case.N), dtype=torch.float32, device=dev)
+    dq, dk, dv = (torch.empty_like(t["q"]) for _ in range(3))
+    if bmask is None:
+        ws = torch.empty(fa.bwd_workspace_bytes(t["q"]), dtype=torch.uint8, device=dev)
+    else:
+        ws = torch.empty(fa.blocksparse_workspace_bytes(t["q"], case.block_size, True), dtype=torch.uint8,
+                         device=dev)
+
+    def step():
+        if bmask is None:
+            fa.fwd(t["q"], t["k"], t["v"], scale=sc, causal=case.causal, key_len=key_len, out=o, lse=lse)
+            fa.bwd(t["q"], t["k"], t["v"], o, t["do"], lse, scale=sc, causal=case.causal, key_len=key_len,
+                   dq=dq, dk=dk, dv=dv, workspace=ws)
+        else:
+            fa.blocksparse_fwd(t["q"], t["k"], t["v"], bmask, case.block_size, scale=sc, out=o, lse=lse,
+                               workspace=ws)
+            fa.blocksparse_bwd(t["q"], t["k"], t["v"], o, t["do"], lse, bmask, case.block_size, scale=sc,
+                               dq=dq, dk=dk, dv=dv, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    pairs = kept_pairs(case)
+    flops_step = 14 * case.d * pairs
+    # MFMA work each kernel executes per launch (the dQ pass recomputes S and dP,
+    # so the two backward kernels together execute 14 d per pair; the step metric
+    # credits only the 10 d of a single-pass backward).
+    kernel_flops = {"fa_fwd_bf16": 4 * case.d * pairs, "fa_bwd_dkdv": 8 * case.d * pairs,
+                    "fa_bwd_dq": 6 * case.d * pairs}
+
+    stream = torch.cuda.current_stream(dev)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with fa.KernelTimer() as timer:
+        torch.cuda.synchronize()
+        start.record(stream)
+        for _ in range(args.steps):
+            step()
+        stop.record(stream)
+        torch.cuda.synchronize()
+        total_ms = start.elapsed_time(stop)
+        kt = {}
+        for name in ("fa_fwd_bf16", "fa_bwd_prep", "fa_bwd_dkdv", "fa_bwd_dq", "fa_block_lists"):
+            ms, n = timer.read(name)
+            if n:
+                kt[name] = {"mean_ms": ms / n, "launches": n, "share": ms / total_ms}
+    ms_step = total_ms / args.steps
+    value = flops_step / (ms_step * 1e-3) / 1e12
+
+    dom = max((k for k in kt if k in kernel_flops), key=lambda k: kt[k]["mean_ms"] * kt[k]["launches"])
+    achieved = kernel_flops[dom] / (kt[dom]["mean_ms"] * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": traffic_for(dom, args.workload)}
+
+    out = {
+        "metric": "attention fwd+bwd TFLOP/s (bf16) and % of MI355X bf16 MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) Q, K, V, dO)",
+        "config": {"workload": f"{args.workload}: {workloads.CONFIGS[args.workload]['desc']}", "B": case.B,
+                   "H": case.H, "N": case.N, "d": case.d, "seed": case.seed,
+                   "mask": "causal" if case.causal else ("block" if bmask is not None else
+                                                         ("key_len" if key_len is not None else "none")),
+                   "kept_pairs": pairs, "flop_per_step": flops_step},
+        "kernels": {k: {"mean_ms": round(v["mean_ms"], 4), "launches": v["launches"],
+                        "share": round(v["share"], 4)} for k, v in kt.items()},
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

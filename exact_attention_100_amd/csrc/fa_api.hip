@@ -133,7 +133,7 @@ size_t round_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
 size_t bwd_ws_bytes(const fa_desc* d) {
   const size_t rows = (size_t)d->B * d->H * d->N;
-  return round_up(rows * d->d * sizeof(float)) + 2 * round_up(rows * sizeof(float));
+  return 2 * round_up(rows * sizeof(float));
 }
 
 size_t lists_bytes(int nb) { return 2 * round_up((size_t)(nb + 1) * 4) + 2 * round_up((size_t)nb * nb * 4); }
@@ -164,8 +164,6 @@ Lists carve_lists(void* ws, int nb) {
 void carve_bwd(const fa_desc* d, void* ws, BwdArgs& a) {
   const size_t rows = (size_t)d->B * d->H * d->N;
   char* p = static_cast<char*>(ws);
-  a.dq_acc = reinterpret_cast<float*>(p);
-  p += round_up(rows * d->d * sizeof(float));
   a.delta = reinterpret_cast<float*>(p);
   p += round_up(rows * sizeof(float));
   a.lse2 = reinterpret_cast<float*>(p);
@@ -318,6 +316,8 @@ extern "C" int fa_blocksparse_bwd(const fa_desc* desc, const void* Q, const void
   if (e != hipSuccess) return FA_ERR_HIP;
   BwdArgs a = bwd_args(desc, Q, K, V, O, dO, LSE, scale, 0, nullptr, dQ, dK, dV);
   carve_bwd(desc, static_cast<char*>(workspace) + lb, a);
+  a.row_ptr = l.row_ptr;
+  a.col_idx = l.col_idx;
   a.col_ptr = l.col_ptr;
   a.row_idx = l.row_idx;
   a.block_size = block_size;

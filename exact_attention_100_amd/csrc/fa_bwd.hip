@@ -10,11 +10,15 @@
 //   dV = P^T dO,  dP = dO V^T,  dS = P o (dP - D),  dQ = scale dS K,  dK = scale dS^T Q.
 //
 // Kernels (same stream):
-//   bwd_prep:     D and LSE * log2(e) per row; clears the f32 dQ accumulator.
-//   bwd_main:     one workgroup per (instance, 128-key block); 4 waves x 32 keys.
-//                 dK and dV of its keys stay in registers across the loop over
-//                 32-query tiles; dQ partials are added to the f32 accumulator.
-//   bwd_dq_store: dQ = scale * accumulator, rounded to bf16.
+//   bwd_prep:  D and LSE log2(e) per row.
+//   bwd_dkdv:  one workgroup per (instance, 128-key block), 4 waves x 32 keys; dK
+//              and dV of its keys stay in registers while it streams the query
+//              tiles that may see them.
+//   bwd_dq:    one workgroup per (instance, 128-query block), 4 waves x 32 queries;
+//              dQ stays in registers while it streams the key tiles its rows see.
+// dQ is computed in its own pass (recomputing S and dP there) rather than
+// accumulated across key blocks with atomics: each output is written once, by
+// one workgroup, so the result is deterministic and no f32 accumulator is needed.
 #include "fa_common.hpp"
 #include "fa_internal.hpp"
 
@@ -30,7 +34,6 @@ struct BwdKParams {
   bf16* dq;
   bf16* dk;
   bf16* dv;
-  float* dq_acc;
   float* delta;
   float* lse2;
   int64_t sb, sh, sn;
@@ -39,19 +42,24 @@ struct BwdKParams {
   float scale;
   int causal;
   const int32_t* key_len;
-  const int32_t* col_ptr;
+  const int32_t* row_ptr;  // block-sparse: kept key blocks per query block
+  const int32_t* col_idx;
+  const int32_t* col_ptr;  // block-sparse: kept query blocks per key block
   const int32_t* row_idx;
   int bs;
-  int n_kblocks;
+  int n_blocks;            // 128-row blocks of N
 };
 
-constexpr int kBwdKeys = 128;   // keys per workgroup
-constexpr int kBwdQ = 32;       // queries per inner tile
+constexpr int kBwdBlock = 128;  // keys (dK/dV pass) or queries (dQ pass) per workgroup
+
+#ifndef FA_BWD_WAVES_PER_EU
+#define FA_BWD_WAVES_PER_EU 2
+#endif
 
 // ------------------------------------------------------------------------------ prep
 
-// One row per D/8 threads: D = sum_i dO_i O_i (f32), lse2 = LSE log2(e) (+inf when
-// the row has no key so that recomputed probabilities are 0), dQ accumulator = 0.
+// One row per D/8 threads: D = sum_i dO_i O_i (f32); lse2 = LSE log2(e), or +inf
+// when the row has no key so that recomputed probabilities are 0.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdKParams p) {
   constexpr int TPR = D / 8;
@@ -69,9 +77,6 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdKParams p) {
     const bf16x8 dv = *reinterpret_cast<const bf16x8*>(p.dout + off);
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc = fmaf((float)ov[i], (float)dv[i], acc);
-    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    *reinterpret_cast<f32x4*>(p.dq_acc + row * D + 8 * sub) = z;
-    *reinterpret_cast<f32x4*>(p.dq_acc + row * D + 8 * sub + 4) = z;
   }
 #pragma unroll
   for (int off = TPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
@@ -82,34 +87,42 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdKParams p) {
   }
 }
 
-// ------------------------------------------------------------------------------ main
+// ------------------------------------------------------------------------------ dK, dV
 
-template <int D, bool SPARSE>
-__global__ __launch_bounds__(256) void bwd_main_kernel(BwdKParams p) {
-  constexpr int QP = D + 8;         // row-major Q / dO tile stride
-  constexpr int TP = kBwdQ + 4;     // transposed Q / dO tile stride
-  constexpr int SP = kBwdKeys + 8;  // dS tile stride ([query][key])
-  constexpr int KTP = kBwdKeys + 8; // K^T stride ([dim][key])
+// Query rows per tile of the dK/dV pass.
+#ifndef FA_BWD_TILE_Q
+#define FA_BWD_TILE_Q 32
+#endif
+
+// Per query tile of BRQ rows (double-buffered in LDS by direct copies, one
+// barrier per tile), each wave, for its 32 keys:
+//   S = Q K_w^T, dP = dO V_w^T   (A = Q / dO rows from LDS, B = K_w / V_w in VGPRs);
+//   P = 2^(c S - lse2), dS = P (dP - D);
+//   dV^T += dO^T P, dK^T += Q^T dS   (A = dO^T / Q^T through transposing LDS reads).
+// Loads past the end are clamped to the last row: such queries have lse2 = +inf
+// (P = 0) and such keys are masked (P = 0); their outputs are not stored.
+// VLDS: the key block's V stays in LDS (read as the B operand of dP) instead of
+// VGPRs, which keeps the d = 128 kernel within 256 registers (two waves per SIMD).
+template <int D, int BRQ, bool SPARSE, bool VLDS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FA_BWD_WAVES_PER_EU)))
+void bwd_dkdv_kernel(BwdKParams p) {
+  constexpr int NQB = BRQ / 32;
   constexpr int NDB = D / 32;
   constexpr int NKK = D / 16;
-  constexpr int QGROUPS = kBwdQ * D / 8 / 256;     // (4 queries x 2 dims) groups per thread
-  constexpr int KGROUPS = kBwdKeys * D / 8 / 256;  // (4 keys x 2 dims) groups per thread
-  static_assert(QGROUPS >= 1 && KGROUPS >= 1, "tile too small");
+  constexpr int TILE = BRQ * D;
+  static_assert(BRQ <= 64, "row statistics use one 64-lane copy");
 
-  __shared__ __attribute__((aligned(16))) bf16 sQ[kBwdQ * QP];
-  __shared__ __attribute__((aligned(16))) bf16 sdO[kBwdQ * QP];
-  __shared__ __attribute__((aligned(16))) bf16 sQt[D * TP];
-  __shared__ __attribute__((aligned(16))) bf16 sdOt[D * TP];
-  __shared__ __attribute__((aligned(16))) bf16 sdS[kBwdQ * SP];
-  __shared__ __attribute__((aligned(16))) bf16 sKt[D * KTP];
-  __shared__ __attribute__((aligned(16))) float sL[kBwdQ];
-  __shared__ __attribute__((aligned(16))) float sDl[kBwdQ];
+  __shared__ __attribute__((aligned(16))) bf16 sQ[2][TILE];
+  __shared__ __attribute__((aligned(16))) bf16 sdO[2][TILE];
+  __shared__ __attribute__((aligned(16))) float sL[2][64];
+  __shared__ __attribute__((aligned(16))) float sDl[2][64];
+  __shared__ __attribute__((aligned(16))) bf16 sV[VLDS ? kBwdBlock * D : 8];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5;
   const int N = p.N;
   int inst, rank;
-  schedule_tile(blockIdx.x, p.B * p.H, p.n_kblocks, inst, rank);
+  schedule_tile(blockIdx.x, p.B * p.H, p.n_blocks, inst, rank);
   const int kb = rank;  // causal: the lowest key blocks see the most queries; they go first
   const int b = inst / p.H, h = inst - b * p.H;
   const int64_t base = (int64_t)b * p.sb + (int64_t)h * p.sh;
@@ -117,7 +130,7 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdKParams p) {
   const bf16* Kh = p.k + base;
   const bf16* Vh = p.v + base;
   const bf16* dOh = p.dout + base;
-  const int k0 = kb * kBwdKeys;
+  const int k0 = kb * kBwdBlock;
   const int kw0 = k0 + 32 * wave;  // this wave's 32 keys
   const int mykey = kw0 + l32;     // the key of this lane's MFMA column
   const int64_t rowbase = (int64_t)inst * N;
@@ -130,19 +143,19 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdKParams p) {
   if (SPARSE) {
     const int kbs = k0 / p.bs;
     cbeg = p.col_ptr[kbs];
-    n_qt = (p.col_ptr[kbs + 1] - cbeg) * (p.bs / kBwdQ);
+    n_qt = (p.col_ptr[kbs + 1] - cbeg) * (p.bs / BRQ);
   } else if (k0 >= kv_len) {
     n_qt = 0;
   } else {
-    qt_begin = p.causal ? k0 / kBwdQ : 0;
-    n_qt = (N + kBwdQ - 1) / kBwdQ - qt_begin;
+    qt_begin = p.causal ? k0 / BRQ : 0;
+    n_qt = (N + BRQ - 1) / BRQ - qt_begin;
   }
   auto tile_q0 = [&](int t) -> int {
     if (SPARSE) {
-      const int tpb = p.bs / kBwdQ;
-      return p.row_idx[cbeg + t / tpb] * p.bs + (t - (t / tpb) * tpb) * kBwdQ;
+      const int tpb = p.bs / BRQ;
+      return p.row_idx[cbeg + t / tpb] * p.bs + (t - (t / tpb) * tpb) * BRQ;
     }
-    return (qt_begin + t) * kBwdQ;
+    return (qt_begin + t) * BRQ;
   };
 
   f32x16 dkacc[NDB], dvacc[NDB];
@@ -157,163 +170,116 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdKParams p) {
   if (n_qt > 0) {
     // This wave's K and V as B operands of S = Q K^T and dP = dO V^T: lane
     // column = mykey; slot group g of k-step kk holds dims [16 kk + 8 g, +8).
-    bf16x8 kf[NKK], vf[NKK];
-    const u32x4 zero4 = {0u, 0u, 0u, 0u};
+    bf16x8 kf[NKK], vf[VLDS ? 1 : NKK];
+    const int64_t koff = (int64_t)min(mykey, N - 1) * p.sn + 8 * g;
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      const int64_t off = (int64_t)mykey * p.sn + 16 * kk + 8 * g;
-      kf[kk] = mykey < N ? *reinterpret_cast<const bf16x8*>(Kh + off) : __builtin_bit_cast(bf16x8, zero4);
-      vf[kk] = mykey < N ? *reinterpret_cast<const bf16x8*>(Vh + off) : __builtin_bit_cast(bf16x8, zero4);
-    }
-    // K^T of the whole key block, for dQ = dS K.
+    for (int kk = 0; kk < NKK; ++kk) kf[kk] = *reinterpret_cast<const bf16x8*>(Kh + koff + 16 * kk);
+    if constexpr (VLDS) {
+      // keys past the end are clamped (their P is 0)
+      tile_dma<kBwdBlock, D, 4>(sV, Vh, p.sn, k0, N, wave, lane);
+    } else {
 #pragma unroll
-    for (int i = 0; i < KGROUPS; ++i) {
-      const int gi = tid + 256 * i, kq = gi / (D / 2), dc = gi - kq * (D / 2);
-      uint32_t w[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int key = k0 + 4 * kq + j;
-        w[j] = key < N ? *reinterpret_cast<const uint32_t*>(Kh + (int64_t)key * p.sn + 2 * dc) : 0u;
-      }
-      u32x2 xs, ys;
-      split_pairs4(w[0], w[1], w[2], w[3], xs, ys);
-      *reinterpret_cast<u32x2*>(&sKt[(2 * dc) * KTP + 4 * kq]) = xs;
-      *reinterpret_cast<u32x2*>(&sKt[(2 * dc + 1) * KTP + 4 * kq]) = ys;
+      for (int kk = 0; kk < NKK; ++kk) vf[kk] = *reinterpret_cast<const bf16x8*>(Vh + koff + 16 * kk);
     }
 
-    // dQ work split: D = 128: wave w owns dims [32 w, 32 w + 32) over all 128 keys;
-    // D = 64: dims 32 (w & 1), keys [64 (w >> 1), +64).
-    constexpr int DQ_KSTEPS = (D == 128) ? 8 : 4;
-    const int dq_db = (D == 128) ? wave : (wave & 1);
-    const int dq_k0 = (D == 128) ? 0 : 64 * (wave >> 1);
+    auto issue_tile = [&](int q0, int buf) {
+      tile_dma<BRQ, D, 4>(sQ[buf], Qh, p.sn, q0, N, wave, lane);
+      tile_dma<BRQ, D, 4>(sdO[buf], dOh, p.sn, q0, N, wave, lane);
+      if (wave == 0) vec_dma64(sL[buf], p.lse2 + rowbase, q0, N, lane);
+      if (wave == 1) vec_dma64(sDl[buf], p.delta + rowbase, q0, N, lane);
+    };
+
+    issue_tile(tile_q0(0), 0);
+    wait_vmem();
+    __syncthreads();
 
     for (int t = 0; t < n_qt; ++t) {
+      const int cur = t & 1;
       const int q0 = tile_q0(t);
-      // Stage Q_i and dO_i (row-major and transposed), lse2_i and D_i.
-#pragma unroll
-      for (int i = 0; i < QGROUPS; ++i) {
-        const int gi = tid + 256 * i, qq = gi / (D / 2), dc = gi - qq * (D / 2);
-        uint32_t wq[4], wd[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int qi = q0 + 4 * qq + j;
-          const int64_t off = (int64_t)qi * p.sn + 2 * dc;
-          wq[j] = qi < N ? *reinterpret_cast<const uint32_t*>(Qh + off) : 0u;
-          wd[j] = qi < N ? *reinterpret_cast<const uint32_t*>(dOh + off) : 0u;
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          *reinterpret_cast<uint32_t*>(&sQ[(4 * qq + j) * QP + 2 * dc]) = wq[j];
-          *reinterpret_cast<uint32_t*>(&sdO[(4 * qq + j) * QP + 2 * dc]) = wd[j];
-        }
-        u32x2 xs, ys;
-        split_pairs4(wq[0], wq[1], wq[2], wq[3], xs, ys);
-        *reinterpret_cast<u32x2*>(&sQt[(2 * dc) * TP + 4 * qq]) = xs;
-        *reinterpret_cast<u32x2*>(&sQt[(2 * dc + 1) * TP + 4 * qq]) = ys;
-        split_pairs4(wd[0], wd[1], wd[2], wd[3], xs, ys);
-        *reinterpret_cast<u32x2*>(&sdOt[(2 * dc) * TP + 4 * qq]) = xs;
-        *reinterpret_cast<u32x2*>(&sdOt[(2 * dc + 1) * TP + 4 * qq]) = ys;
-      }
-      if (tid < kBwdQ) {
-        const int qi = q0 + tid;
-        sL[tid] = qi < N ? p.lse2[rowbase + qi] : kPosInf;
-        sDl[tid] = qi < N ? p.delta[rowbase + qi] : 0.f;
-      }
-      __syncthreads();
+      // Prefetch the next tile into the idle buffer (the last iteration re-reads
+      // its own tile); every wave finished reading that buffer before the
+      // previous barrier.
+      issue_tile(tile_q0(min(t + 1, n_qt - 1)), cur ^ 1);
 
       // S = Q_i K_w^T and dP = dO_i V_w^T (rows = queries, columns = this wave's keys).
-      f32x16 sacc, dpacc;
+      f32x16 sacc[NQB], dpacc[NQB];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        sacc[r] = 0.f;
-        dpacc[r] = 0.f;
-      }
+      for (int sb = 0; sb < NQB; ++sb)
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        const bf16x8 aq = *reinterpret_cast<const bf16x8*>(&sQ[l32 * QP + 16 * kk + 8 * g]);
-        const bf16x8 ad = *reinterpret_cast<const bf16x8*>(&sdO[l32 * QP + 16 * kk + 8 * g]);
-        sacc = mfma_bf16(aq, kf[kk], sacc);
-        dpacc = mfma_bf16(ad, vf[kk], dpacc);
-      }
-
-      // P = 2^(c S - lse2), dS = P (dP - D). Register r is query q0 + 8 (r/4) + 4 g + r%4.
-      const bool need_mask =
-          !SPARSE && ((p.causal && q0 < kw0 + 31) || (kw0 + 32 > kv_len) || (q0 + kBwdQ > N));
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const f32x4 lv = *reinterpret_cast<const f32x4*>(&sL[8 * j + 4 * g]);
-        const f32x4 dv = *reinterpret_cast<const f32x4*>(&sDl[8 * j + 4 * g]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 4 * j + i;
-          float pr = fast_exp2(fmaf(sacc[r], p.c, -lv[i]));
-          if (need_mask) {
-            const int qi = q0 + 8 * j + 4 * g + i;
-            const bool ok = mykey < kv_len && qi < N && (!p.causal || mykey <= qi);
-            if (!ok) pr = 0.f;
-          }
-          sacc[r] = pr;
-          dpacc[r] = pr * (dpacc[r] - dv[i]);
+        for (int r = 0; r < 16; ++r) {
+          sacc[sb][r] = 0.f;
+          dpacc[sb][r] = 0.f;
         }
-      }
-
-      // P and dS as B operands (column = key, K = queries): k-step s covers queries
-      // 16 s + {4g..4g+3, 8+4g..8+4g+3}, i.e. registers 8 s .. 8 s + 7.
-      bf16x8 pb[2], dsb[2];
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        pb[s] = pack_bf16x8(sacc[8 * s + 0], sacc[8 * s + 1], sacc[8 * s + 2], sacc[8 * s + 3],
-                            sacc[8 * s + 4], sacc[8 * s + 5], sacc[8 * s + 6], sacc[8 * s + 7]);
-        dsb[s] = pack_bf16x8(dpacc[8 * s + 0], dpacc[8 * s + 1], dpacc[8 * s + 2], dpacc[8 * s + 3],
-                             dpacc[8 * s + 4], dpacc[8 * s + 5], dpacc[8 * s + 6], dpacc[8 * s + 7]);
-      }
+      for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+        for (int sb = 0; sb < NQB; ++sb) {
+          const int off = tile_off<D>(32 * sb + l32, 16 * kk + 8 * g);
+          bf16x8 vb;
+          if constexpr (VLDS)
+            vb = *reinterpret_cast<const bf16x8*>(&sV[tile_off<D>(32 * wave + l32, 16 * kk + 8 * g)]);
+          else
+            vb = vf[kk];
+          sacc[sb] = mfma_bf16(*reinterpret_cast<const bf16x8*>(&sQ[cur][off]), kf[kk], sacc[sb]);
+          dpacc[sb] = mfma_bf16(*reinterpret_cast<const bf16x8*>(&sdO[cur][off]), vb, dpacc[sb]);
+        }
+
+      // P = 2^(c S - lse2), dS = P (dP - D). Register r of sub-block sb is query
+      // q0 + 32 sb + 8 (r/4) + 4 g + r%4. Rows past N carry lse2 = +inf (P = 0)
+      // only when they exist in the loaded statistics, so they are masked too.
+      const bool need_mask =
+          !SPARSE && ((p.causal && q0 < kw0 + 31) || (kw0 + 32 > kv_len) || (q0 + BRQ > N));
+#pragma unroll
+      for (int sb = 0; sb < NQB; ++sb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const f32x4 lv = *reinterpret_cast<const f32x4*>(&sL[cur][32 * sb + 8 * j + 4 * g]);
+          const f32x4 dv = *reinterpret_cast<const f32x4*>(&sDl[cur][32 * sb + 8 * j + 4 * g]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = 4 * j + i;
+            float pr = fast_exp2(fmaf(sacc[sb][r], p.c, -lv[i]));
+            if (need_mask) {
+              const int qi = q0 + 32 * sb + 8 * j + 4 * g + i;
+              const bool ok = mykey < kv_len && qi < N && (!p.causal || mykey <= qi);
+              if (!ok) pr = 0.f;
+            }
+            sacc[sb][r] = pr;
+            dpacc[sb][r] = pr * (dpacc[sb][r] - dv[i]);
+          }
+        }
+
+      // P and dS as B operands (column = key, K index = query): query step qs =
+      // 2 sb + s covers queries 32 sb + 16 s + {4g..4g+3, 8+4g..8+4g+3}, i.e.
+      // registers 8 s .. 8 s + 7 of sub-block sb.
+      bf16x8 pb[2 * NQB], dsb[2 * NQB];
+#pragma unroll
+      for (int sb = 0; sb < NQB; ++sb)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const f32x16& P = sacc[sb];
+          const f32x16& S = dpacc[sb];
+          pb[2 * sb + s] = pack_bf16x8(P[8 * s], P[8 * s + 1], P[8 * s + 2], P[8 * s + 3], P[8 * s + 4],
+                                       P[8 * s + 5], P[8 * s + 6], P[8 * s + 7]);
+          dsb[2 * sb + s] = pack_bf16x8(S[8 * s], S[8 * s + 1], S[8 * s + 2], S[8 * s + 3], S[8 * s + 4],
+                                        S[8 * s + 5], S[8 * s + 6], S[8 * s + 7]);
+        }
 
       // dV^T += dO^T P and dK^T += Q^T dS (rows = dims, columns = this wave's keys).
 #pragma unroll
-      for (int s = 0; s < 2; ++s)
+      for (int qs = 0; qs < 2 * NQB; ++qs)
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          const bf16* ap = &sdOt[(db * 32 + l32) * TP + 16 * s + 4 * g];
-          const bf16* aq = &sQt[(db * 32 + l32) * TP + 16 * s + 4 * g];
-          const bf16x8 a_do = concat_bf16x4(*reinterpret_cast<const bf16x4*>(ap),
-                                            *reinterpret_cast<const bf16x4*>(ap + 8));
-          const bf16x8 a_q = concat_bf16x4(*reinterpret_cast<const bf16x4*>(aq),
-                                           *reinterpret_cast<const bf16x4*>(aq + 8));
-          dvacc[db] = mfma_bf16(a_do, pb[s], dvacc[db]);
-          dkacc[db] = mfma_bf16(a_q, dsb[s], dkacc[db]);
+          dvacc[db] = mfma_bf16(lds_read_tr_k16_swz<D>(sdO[cur], 16 * qs, 32 * db, lane), pb[qs], dvacc[db]);
+          dkacc[db] = mfma_bf16(lds_read_tr_k16_swz<D>(sQ[cur], 16 * qs, 32 * db, lane), dsb[qs], dkacc[db]);
         }
 
-      // dS to LDS as [query][key] for dQ.
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        sdS[(8 * (r >> 2) + 4 * g + (r & 3)) * SP + 32 * wave + l32] = (bf16)dpacc[r];
+      wait_vmem();
       __syncthreads();
-
-      // dQ_i[:, dims] += dS_i K[keys, dims]: A = dS rows (query), B = K^T rows (dim),
-      // slot group g of k-step ks holds keys [16 ks + 8 g, +8).
-      f32x16 dqacc;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) dqacc[r] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < DQ_KSTEPS; ++ks) {
-        const int kc = dq_k0 + 16 * ks + 8 * g;
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sdS[l32 * SP + kc]);
-        const bf16x8 bk = *reinterpret_cast<const bf16x8*>(&sKt[(dq_db * 32 + l32) * KTP + kc]);
-        dqacc = mfma_bf16(a, bk, dqacc);
-      }
-      float* dqrow = p.dq_acc + (rowbase + q0) * D + dq_db * 32 + l32;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int qo = 8 * (r >> 2) + 4 * g + (r & 3);
-        if (q0 + qo < N) unsafeAtomicAdd(dqrow + (int64_t)qo * D, dqacc[r]);
-      }
-      // The next tile's staging only touches buffers that every wave finished
-      // reading before the barrier above; sdS is rewritten only after the next
-      // tile's first barrier.
     }
   }
 
-  // dK = scale dK^T^T, dV: lane column = mykey, register r = dim 32 db + 8 (r/4) + 4 g + r%4.
+  // dK = scale (dK^T)^T, dV: lane column = mykey, register r = dim 32 db + 8 (r/4) + 4 g + r%4.
   if (mykey < N) {
     bf16* dkrow = p.dk + base + (int64_t)mykey * p.sn;
     bf16* dvrow = p.dv + base + (int64_t)mykey * p.sn;
@@ -332,26 +298,170 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdKParams p) {
   }
 }
 
-// ------------------------------------------------------------------------------ dQ store
+// ------------------------------------------------------------------------------ dQ
 
-template <int D>
-__global__ __launch_bounds__(256) void bwd_dq_store_kernel(BwdKParams p) {
-  const int64_t chunk = (int64_t)blockIdx.x * 256 + threadIdx.x;  // 8 elements each
-  const int64_t total = (int64_t)p.B * p.H * p.N * (D / 8);
-  if (chunk >= total) return;
-  const int64_t row = chunk / (D / 8);
-  const int c8 = (int)(chunk - row * (D / 8)) * 8;
-  const int64_t inst = row / p.N;
-  const int n = (int)(row - inst * p.N);
-  const int b = (int)(inst / p.H), h = (int)(inst - (int64_t)b * p.H);
-  const f32x4 a0 = *reinterpret_cast<const f32x4*>(p.dq_acc + row * D + c8);
-  const f32x4 a1 = *reinterpret_cast<const f32x4*>(p.dq_acc + row * D + c8 + 4);
-  u32x4 w;
-  w[0] = pack_bf16x2(a0[0] * p.scale, a0[1] * p.scale);
-  w[1] = pack_bf16x2(a0[2] * p.scale, a0[3] * p.scale);
-  w[2] = pack_bf16x2(a1[0] * p.scale, a1[1] * p.scale);
-  w[3] = pack_bf16x2(a1[2] * p.scale, a1[3] * p.scale);
-  *reinterpret_cast<u32x4*>(p.dq + (int64_t)b * p.sb + (int64_t)h * p.sh + (int64_t)n * p.sn + c8) = w;
+// Keys per tile of the dQ pass, per head dim (32 keeps d = 128 within 256 registers).
+#ifndef FA_BWD_TILE_K_D128
+#define FA_BWD_TILE_K_D128 32
+#endif
+#ifndef FA_BWD_TILE_K_D64
+#define FA_BWD_TILE_K_D64 64
+#endif
+
+// Per key tile of BC keys (double-buffered in LDS by direct copies), each wave,
+// for its 32 queries (one query per lane column, as in the forward):
+//   S^T = K Q^T, dP^T = V dO^T     (A = K / V rows from LDS, B = Q / dO in VGPRs);
+//   P^T = 2^(c S^T - lse2_q), dS^T = P^T (dP^T - D_q)   (one lse2, D per lane);
+//   dQ^T += K^T dS^T               (A = K^T through the transposing LDS read,
+//                                   B = dS^T straight from the accumulator layout).
+// Loads past the end are clamped to the last row: such keys are masked (P = 0)
+// and such queries are not stored.
+template <int D, int BC, bool SPARSE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FA_BWD_WAVES_PER_EU)))
+void bwd_dq_kernel(BwdKParams p) {
+  constexpr int NKB = BC / 32;
+  constexpr int NDB = D / 32;
+  constexpr int NKK = D / 16;
+  constexpr int TILE = BC * D;
+
+  __shared__ __attribute__((aligned(16))) bf16 sK[2][TILE];
+  __shared__ __attribute__((aligned(16))) bf16 sV[2][TILE];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, g = lane >> 5;
+  const int N = p.N;
+  int inst, rank;
+  schedule_tile(blockIdx.x, p.B * p.H, p.n_blocks, inst, rank);
+  const int qb = (!SPARSE && p.causal) ? (p.n_blocks - 1 - rank) : rank;  // heaviest causal rows first
+  const int b = inst / p.H, h = inst - b * p.H;
+  const int64_t base = (int64_t)b * p.sb + (int64_t)h * p.sh;
+  const bf16* Qh = p.q + base;
+  const bf16* Kh = p.k + base;
+  const bf16* Vh = p.v + base;
+  const bf16* dOh = p.dout + base;
+  const int q0 = qb * kBwdBlock;
+  const int qrow = q0 + 32 * wave + l32;
+  const int qc = min(qrow, N - 1);
+  const int64_t rowbase = (int64_t)inst * N;
+
+  // The key tiles this query block visits (as in the forward).
+  int kv_len = N, n_tiles, blk_begin = 0;
+  if (SPARSE) {
+    const int rb = q0 / p.bs;
+    blk_begin = p.row_ptr[rb];
+    n_tiles = (p.row_ptr[rb + 1] - blk_begin) * (p.bs / BC);
+  } else {
+    if (p.key_len) kv_len = min(max(p.key_len[b], 0), N);
+    int kv_end = kv_len;
+    if (p.causal) kv_end = min(kv_end, q0 + kBwdBlock);
+    n_tiles = kv_end > 0 ? (kv_end + BC - 1) / BC : 0;
+  }
+  auto tile_kv0 = [&](int t) -> int {
+    if (SPARSE) {
+      if (t >= n_tiles) return 0;
+      const int tpb = p.bs / BC;
+      return p.col_idx[blk_begin + t / tpb] * p.bs + (t - (t / tpb) * tpb) * BC;
+    }
+    return t * BC;
+  };
+
+  // This lane's query row of Q and dO as B operands (dims [16 kk + 8 g, +8)),
+  // and its row statistics.
+  bf16x8 qf[NKK], df[NKK];
+  const int64_t qoff = (int64_t)qc * p.sn + 8 * g;
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) {
+    qf[kk] = *reinterpret_cast<const bf16x8*>(Qh + qoff + 16 * kk);
+    df[kk] = *reinterpret_cast<const bf16x8*>(dOh + qoff + 16 * kk);
+  }
+  const float lse2_q = p.lse2[rowbase + qc];
+  const float d_q = p.delta[rowbase + qc];
+
+  f32x16 dqacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dqacc[db][r] = 0.f;
+
+  auto issue_tile = [&](int kv0, int buf) {
+    tile_dma<BC, D, 4>(sK[buf], Kh, p.sn, kv0, N, wave, lane);
+    tile_dma<BC, D, 4>(sV[buf], Vh, p.sn, kv0, N, wave, lane);
+  };
+  issue_tile(tile_kv0(0), 0);
+  wait_vmem();
+  __syncthreads();
+
+  for (int t = 0; t < n_tiles; ++t) {
+    const int buf = t & 1;
+    const int kv0 = tile_kv0(t);
+    issue_tile(tile_kv0(min(t + 1, n_tiles - 1)), buf ^ 1);
+
+    // S^T and dP^T (keys x queries).
+    f32x16 sacc[NKB], dpacc[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        sacc[kb][r] = 0.f;
+        dpacc[kb][r] = 0.f;
+      }
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const int off = tile_off<D>(32 * kb + l32, 16 * kk + 8 * g);
+        sacc[kb] = mfma_bf16(*reinterpret_cast<const bf16x8*>(&sK[buf][off]), qf[kk], sacc[kb]);
+        dpacc[kb] = mfma_bf16(*reinterpret_cast<const bf16x8*>(&sV[buf][off]), df[kk], dpacc[kb]);
+      }
+
+    // dS^T = P^T (dP^T - D); register r of block kb is key kv0 + 32 kb + 8 (r/4) + 4 g + r%4.
+    const bool need_mask = !SPARSE && ((kv0 + BC > kv_len) || (p.causal && kv0 + BC - 1 > q0 + 32 * wave));
+    bf16x8 dsb[2 * NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float pr = fast_exp2(fmaf(sacc[kb][r], p.c, -lse2_q));
+        if (need_mask) {
+          const int key = kv0 + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
+          const bool ok = key < kv_len && (!p.causal || key <= qrow);
+          if (!ok) pr = 0.f;
+        }
+        dpacc[kb][r] = pr * (dpacc[kb][r] - d_q);
+      }
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const f32x16& S = dpacc[kb];
+        dsb[2 * kb + s] = pack_bf16x8(S[8 * s], S[8 * s + 1], S[8 * s + 2], S[8 * s + 3], S[8 * s + 4],
+                                      S[8 * s + 5], S[8 * s + 6], S[8 * s + 7]);
+      }
+    }
+
+    // dQ^T (dims x queries) += K^T dS^T: the K^T slots of k-step ks are keys
+    // 16 ks + {4g..4g+3, 8+4g..8+4g+3}, those of dsb[ks].
+#pragma unroll
+    for (int ks = 0; ks < BC / 16; ++ks)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+        dqacc[db] = mfma_bf16(lds_read_tr_k16_swz<D>(sK[buf], 16 * ks, 32 * db, lane), dsb[ks], dqacc[db]);
+
+    wait_vmem();
+    __syncthreads();
+  }
+
+  // dQ = scale dQ^T^T: lane = query, register r = dim 32 db + 8 (r/4) + 4 g + r%4.
+  if (qrow < N) {
+    bf16* dqrow = p.dq + base + (int64_t)qrow * p.sn;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        u32x2 w;
+        w[0] = pack_bf16x2(dqacc[db][4 * j] * p.scale, dqacc[db][4 * j + 1] * p.scale);
+        w[1] = pack_bf16x2(dqacc[db][4 * j + 2] * p.scale, dqacc[db][4 * j + 3] * p.scale);
+        *reinterpret_cast<u32x2*>(dqrow + db * 32 + 8 * j + 4 * g) = w;
+      }
+  }
 }
 
 // ------------------------------------------------------------------------------ launcher
@@ -367,7 +477,6 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s) {
   p.dq = static_cast<bf16*>(a.dq);
   p.dk = static_cast<bf16*>(a.dk);
   p.dv = static_cast<bf16*>(a.dv);
-  p.dq_acc = a.dq_acc;
   p.delta = a.delta;
   p.lse2 = a.lse2;
   p.sb = a.sb;
@@ -380,10 +489,12 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s) {
   p.c = a.scale * kLog2e;
   p.causal = a.causal;
   p.key_len = a.key_len;
+  p.row_ptr = a.row_ptr;
+  p.col_idx = a.col_idx;
   p.col_ptr = a.col_ptr;
   p.row_idx = a.row_idx;
   p.bs = a.block_size;
-  p.n_kblocks = (a.N + kBwdKeys - 1) / kBwdKeys;
+  p.n_blocks = (a.N + kBwdBlock - 1) / kBwdBlock;
   const bool sparse = a.col_ptr != nullptr;
   const int64_t rows = (int64_t)a.B * a.H * a.N;
   const dim3 block(256);
@@ -397,24 +508,28 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
-  const dim3 grid_main((unsigned)(a.B * a.H * p.n_kblocks));
-  timer_begin("fa_bwd_main", s);
+  constexpr int TQ = FA_BWD_TILE_Q, TK128 = FA_BWD_TILE_K_D128, TK64 = FA_BWD_TILE_K_D64;
+  const dim3 grid((unsigned)(a.B * a.H * p.n_blocks));
+  timer_begin("fa_bwd_dkdv", s);
   if (a.d == 128) {
-    if (sparse) bwd_main_kernel<128, true><<<grid_main, block, 0, s>>>(p);
-    else bwd_main_kernel<128, false><<<grid_main, block, 0, s>>>(p);
+    if (sparse) bwd_dkdv_kernel<128, TQ, true, true><<<grid, block, 0, s>>>(p);
+    else bwd_dkdv_kernel<128, TQ, false, true><<<grid, block, 0, s>>>(p);
   } else {
-    if (sparse) bwd_main_kernel<64, true><<<grid_main, block, 0, s>>>(p);
-    else bwd_main_kernel<64, false><<<grid_main, block, 0, s>>>(p);
+    if (sparse) bwd_dkdv_kernel<64, TQ, true, false><<<grid, block, 0, s>>>(p);
+    else bwd_dkdv_kernel<64, TQ, false, false><<<grid, block, 0, s>>>(p);
   }
   timer_end(s);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
 
-  const int64_t chunks = rows * (a.d / 8);
-  const dim3 grid_store((unsigned)((chunks + 255) / 256));
-  timer_begin("fa_bwd_dq_store", s);
-  if (a.d == 128) bwd_dq_store_kernel<128><<<grid_store, block, 0, s>>>(p);
-  else bwd_dq_store_kernel<64><<<grid_store, block, 0, s>>>(p);
+  timer_begin("fa_bwd_dq", s);
+  if (a.d == 128) {
+    if (sparse) bwd_dq_kernel<128, TK128, true><<<grid, block, 0, s>>>(p);
+    else bwd_dq_kernel<128, TK128, false><<<grid, block, 0, s>>>(p);
+  } else {
+    if (sparse) bwd_dq_kernel<64, TK64, true><<<grid, block, 0, s>>>(p);
+    else bwd_dq_kernel<64, TK64, false><<<grid, block, 0, s>>>(p);
+  }
   timer_end(s);
   return hipGetLastError();
 }

@@ -75,9 +75,17 @@ __device__ __forceinline__ bf16x8 concat_bf16x4(bf16x4 lo, bf16x4 hi) {
   return __builtin_bit_cast(bf16x8, u);
 }
 
-// Value held by lane (l ^ 32): the lane holding the same MFMA column in the
-// other lane group.
-__device__ __forceinline__ float other_half(float x) { return __shfl_xor(x, 32, 64); }
+// Combine a value with the one held by lane (l ^ 32), the lane holding the same
+// MFMA column in the other lane group, through v_permlane32_swap (lanes < 32 get
+// {own, partner}, lanes >= 32 get {partner, own}; max and sum are symmetric).
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 // Build the low/high bf16 halves of four packed bf16 pairs into two 4-element
 // rows: in[j] = (x_j, y_j) -> xs = (x_0..x_3), ys = (y_0..y_3).
@@ -88,6 +96,89 @@ __device__ __forceinline__ void split_pairs4(uint32_t in0, uint32_t in1, uint32_
   ys[0] = (in0 >> 16) | (in1 & 0xFFFF0000u);
   ys[1] = (in2 >> 16) | (in3 & 0xFFFF0000u);
 }
+
+// Transposing LDS read (ds_read_b64_tr_b16). For a row-major bf16 matrix X[k][m]
+// in LDS with row stride ld (elements), lane l receives the 8 values
+//   X[k0 + kmap(g, s)][m0 + l % 32],  s = 0..7,  g = l / 32,
+//   kmap(g, s) = 4 g + s (s < 4),  8 + 4 g + (s - 4) (s >= 4),
+// i.e. a 32 x 16 operand (rows m, K index k) whose slot order matches the rows of
+// an MFMA accumulator (register r <-> row 8 (r/4) + 4 g + r % 4). The hardware
+// gives lane j of each 16-lane group element (j % 4) of the 8-byte chunks
+// addressed by lanes 4 t + j / 4 (t = 0..3), so the 16 lanes of a group address
+// a 4-row x 16-column block and each receives one of its columns.
+__device__ __forceinline__ bf16x8 lds_read_tr_k16(const bf16* X, int ld, int k0, int m0, int lane) {
+  const int g = lane >> 5, h = (lane >> 4) & 1, j = lane & 15;
+  const bf16* p0 = X + (k0 + 4 * g + (j >> 2)) * ld + m0 + 16 * h + 4 * (j & 3);
+  typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p0));
+  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p0 + 8 * ld));
+  return concat_bf16x4(lo, hi);
+}
+
+// Swizzled row-major LDS tiles. A tile with COLS bf16 columns (COLS / 8 chunks
+// of 16 bytes per row, no padding) stores element (r, c) in chunk
+// (c / 8) ^ tile_swz<COLS>(r) of row r. tile_swz is linear over GF(2) in the low
+// four row bits; the maps below keep three access patterns free of bank
+// conflicts (checked for both 32- and 64-bank LDS models): 16-byte row reads by
+// 16 consecutive rows (MFMA operands), transposing 8-byte reads of 4 rows x 32
+// columns (lds_read_tr_k16_swz) and 16-byte row-major writes.
+template <int COLS>
+__device__ __forceinline__ int tile_swz(int r) {
+  static_assert(COLS == 128 || COLS == 64 || COLS == 32, "unsupported tile width");
+  constexpr int b0 = COLS == 128 ? 4 : (COLS == 64 ? 2 : 0);
+  constexpr int b1 = COLS == 128 ? 10 : (COLS == 64 ? 4 : 2);
+  return ((r & 1) ? b0 : 0) ^ ((r & 2) ? b1 : 0) ^ ((r & 4) ? 1 : 0) ^ ((r & 8) ? 2 : 0);
+}
+template <int COLS>
+__device__ __forceinline__ int tile_off(int r, int c) {
+  return r * COLS + ((((c >> 3) ^ tile_swz<COLS>(r))) << 3) + (c & 7);
+}
+
+// lds_read_tr_k16 on a swizzled tile (same result layout).
+template <int COLS>
+__device__ __forceinline__ bf16x8 lds_read_tr_k16_swz(const bf16* X, int k0, int m0, int lane) {
+  const int g = lane >> 5, h = (lane >> 4) & 1, j = lane & 15;
+  const int r = k0 + 4 * g + (j >> 2), c = m0 + 16 * h + 4 * (j & 3);
+  typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(X + tile_off<COLS>(r, c)));
+  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(X + tile_off<COLS>(r + 8, c)));
+  return concat_bf16x4(lo, hi);
+}
+
+// Direct global -> LDS copy of a [ROWS x COLS] bf16 tile into the swizzled
+// layout above (global_load_lds_dwordx4: lane i of an instruction writes LDS
+// chunk base + i, so each lane fetches the global chunk that belongs there).
+// Global rows row0 + r past nvalid are clamped to row nvalid - 1 (see the
+// callers for why the clamped values are harmless). NWAVES waves share the
+// copy; the caller waits (vmcnt) and synchronises before the tile is read.
+template <int ROWS, int COLS, int NWAVES>
+__device__ __forceinline__ void tile_dma(bf16* lds_tile, const bf16* g, int64_t ld, int row0, int nvalid,
+                                         int wave, int lane) {
+  constexpr int CPR = COLS / 8;
+  constexpr int PER_WAVE = ROWS * CPR / (64 * NWAVES);
+  static_assert(PER_WAVE >= 1 && PER_WAVE * 64 * NWAVES == ROWS * CPR, "tile must split into whole wave copies");
+#pragma unroll
+  for (int i = 0; i < PER_WAVE; ++i) {
+    const int base = (i * NWAVES + wave) * 64;  // first LDS chunk of this copy (wave-uniform)
+    const int pch = base + lane;
+    const int r = pch / CPR, lc = (pch % CPR) ^ tile_swz<COLS>(r);
+    const int64_t grow = min(row0 + r, nvalid - 1);
+    __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(g + grow * ld + 8 * lc),
+                                     (void __attribute__((address_space(3)))*)(lds_tile + 8 * base), 16, 0, 0);
+  }
+}
+
+// Same for a vector of COUNT (<= 64) floats: one copy by one wave; lanes past
+// COUNT write the padding of a 64-float LDS array.
+__device__ __forceinline__ void vec_dma64(float* lds_vec, const float* g, int i0, int nvalid, int lane) {
+  const int64_t gi = min(i0 + lane, nvalid - 1);
+  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(g + gi),
+                                   (void __attribute__((address_space(3)))*)(lds_vec), 4, 0, 0);
+}
+
+// Wait until this wave's outstanding vector-memory operations (including
+// direct-to-LDS copies) have completed: s_waitcnt vmcnt(0).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Workgroup -> (instance, tile) schedule. Consecutive workgroup ids are handed
 // to the 8 XCDs in turn; when the instance count allows it, all tiles of one

@@ -11,8 +11,8 @@
 //
 // gfx950 mapping (our design):
 //   * 4 waves x 32 query rows = 128 rows per workgroup; K/V tiles of BC keys,
-//     double-buffered in LDS (K row-major, V transposed so the PV operand is a
-//     pair of 8-byte LDS reads).
+//     double-buffered row-major in LDS; the V^T operand of P V comes from the
+//     transposing LDS read (ds_read_b64_tr_b16), two per MFMA.
 //   * Each wave computes S^T = K Q^T on the 32x32x16 bf16 MFMA, so a lane owns
 //     ONE query column and 16 keys of it: row max / row sum are per-lane
 //     reductions plus one exchange with lane l^32, the rescale factor is one
@@ -72,6 +72,7 @@ __device__ __forceinline__ FwdRange fwd_range(const FwdKParams& p, int b, int q0
 template <int BC, bool SPARSE>
 __device__ __forceinline__ int fwd_tile_kv0(const FwdKParams& p, const FwdRange& r, int t) {
   if (SPARSE) {
+    if (t >= r.n_tiles) return 0;  // (the prologue of an empty row list)
     const int tpb = p.bs / BC;
     const int blk = p.col_idx[r.blk_begin + t / tpb];
     return blk * p.bs + (t - (t / tpb) * tpb) * BC;
@@ -103,7 +104,7 @@ __device__ __forceinline__ float online_softmax_step(f32x16 (&s)[NKB], bool need
   for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-  mx = fmaxf(mx, other_half(mx));
+  mx = pair_max(mx);
   const float mxs = (mx == kNegInf) ? kNegInf : mx * c;
   const float m_new = fmaxf(m_run, mxs);
   const float m_use = (m_new == kNegInf) ? 0.f : m_new;
@@ -125,19 +126,25 @@ __device__ __forceinline__ float online_softmax_step(f32x16 (&s)[NKB], bool need
 
 // ----------------------------------------------------------------------------------- bf16
 
+// Waves per SIMD the bf16 forward is compiled for: two, so that one wave's
+// softmax (VALU, transcendental) overlaps the other wave's MFMA work.
+#ifndef FA_FWD_WAVES_PER_EU
+#define FA_FWD_WAVES_PER_EU 2
+#endif
+
 template <int D, int BC, bool SPARSE>
-__global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdKParams p) {
-  constexpr int KP = D + 8;   // K tile row stride (elements): 16-byte rows, banks spread
-  constexpr int VP = BC + 4;  // V^T tile row stride
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FA_FWD_WAVES_PER_EU)))
+void fwd_bf16_kernel(FwdKParams p) {
+  constexpr int KP = D + 8;   // K tile row stride: 16-byte rows spread over the banks
+  constexpr int VP = D + 32;  // V tile row stride: the 4 rows of a transposing read hit disjoint banks
   constexpr int NKB = BC / 32;
   constexpr int NDB = D / 32;
   constexpr int NKK = D / 16;
-  constexpr int K_CHUNKS = BC * D / 8 / 256;  // 16-byte chunks of K per thread per tile
-  constexpr int V_GROUPS = BC * D / 8 / 256;  // (4 keys x 2 dims) groups of V per thread
-  static_assert(K_CHUNKS >= 1 && V_GROUPS >= 1, "tile too small for 256 threads");
+  constexpr int CHUNKS = BC * D / 8 / 256;  // 16-byte chunks of K (and of V) per thread per tile
+  static_assert(CHUNKS >= 1, "tile too small for 256 threads");
 
   __shared__ __attribute__((aligned(16))) bf16 sK[2][BC * KP];
-  __shared__ __attribute__((aligned(16))) bf16 sVt[2][D * VP];
+  __shared__ __attribute__((aligned(16))) bf16 sV[2][BC * VP];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5;
@@ -156,45 +163,33 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdKParams p) {
 
   // This lane's query, as the B operand of S^T = K Q^T: slot group g of k-step
   // kk holds dims [16 kk + 8 g, 16 kk + 8 g + 8).
+  // Every global load below is unconditional: row indices past the end are
+  // clamped to row N - 1, whose values then only ever meet probability 0 (masked
+  // keys) or feed outputs that are not stored (query rows >= N). Branch-free
+  // loads let the compiler count outstanding loads exactly, so prefetches stay
+  // in flight across the MFMA work.
   bf16x8 qf[NKK];
-  const u32x4 zero4 = {0u, 0u, 0u, 0u};
+  const int64_t qoff = (int64_t)min(qrow, N - 1) * p.sn;
 #pragma unroll
-  for (int kk = 0; kk < NKK; ++kk)
-    qf[kk] = (qrow < N) ? *reinterpret_cast<const bf16x8*>(Qh + (int64_t)qrow * p.sn + 16 * kk + 8 * g)
-                        : __builtin_bit_cast(bf16x8, zero4);
+  for (int kk = 0; kk < NKK; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(Qh + qoff + 16 * kk + 8 * g);
 
-  u32x4 kreg[K_CHUNKS];
-  uint32_t vreg[V_GROUPS][4];
+  // K and V tiles are staged row-major: 16-byte chunks, D/8 chunks per key.
+  u32x4 kreg[CHUNKS], vreg[CHUNKS];
   auto load_tile = [&](int kv0) {
 #pragma unroll
-    for (int i = 0; i < K_CHUNKS; ++i) {
+    for (int i = 0; i < CHUNKS; ++i) {
       const int ci = tid + 256 * i, r = ci / (D / 8), cc = ci - r * (D / 8);
-      const int key = kv0 + r;
-      kreg[i] = key < N ? *reinterpret_cast<const u32x4*>(Kh + (int64_t)key * p.sn + 8 * cc) : zero4;
-    }
-#pragma unroll
-    for (int i = 0; i < V_GROUPS; ++i) {
-      const int gi = tid + 256 * i, kq = gi / (D / 2), dc = gi - kq * (D / 2);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int key = kv0 + 4 * kq + j;
-        vreg[i][j] = key < N ? *reinterpret_cast<const uint32_t*>(Vh + (int64_t)key * p.sn + 2 * dc) : 0u;
-      }
+      const int64_t off = (int64_t)min(kv0 + r, N - 1) * p.sn + 8 * cc;
+      kreg[i] = *reinterpret_cast<const u32x4*>(Kh + off);
+      vreg[i] = *reinterpret_cast<const u32x4*>(Vh + off);
     }
   };
   auto store_tile = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < K_CHUNKS; ++i) {
+    for (int i = 0; i < CHUNKS; ++i) {
       const int ci = tid + 256 * i, r = ci / (D / 8), cc = ci - r * (D / 8);
       *reinterpret_cast<u32x4*>(&sK[buf][r * KP + 8 * cc]) = kreg[i];
-    }
-#pragma unroll
-    for (int i = 0; i < V_GROUPS; ++i) {
-      const int gi = tid + 256 * i, kq = gi / (D / 2), dc = gi - kq * (D / 2);
-      u32x2 xs, ys;
-      split_pairs4(vreg[i][0], vreg[i][1], vreg[i][2], vreg[i][3], xs, ys);
-      *reinterpret_cast<u32x2*>(&sVt[buf][(2 * dc) * VP + 4 * kq]) = xs;
-      *reinterpret_cast<u32x2*>(&sVt[buf][(2 * dc + 1) * VP + 4 * kq]) = ys;
+      *reinterpret_cast<u32x4*>(&sV[buf][r * VP + 8 * cc]) = vreg[i];
     }
   };
 
@@ -205,16 +200,16 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdKParams p) {
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
   float m_run = kNegInf, l_run = 0.f;
 
-  if (rg.n_tiles > 0) {
-    load_tile(fwd_tile_kv0<BC, SPARSE>(p, rg, 0));
-    store_tile(0);
-  }
+  // The tile loop always prefetches (the last iteration re-reads its own tile
+  // into the idle buffer) so that it has no branches around memory operations.
+  load_tile(fwd_tile_kv0<BC, SPARSE>(p, rg, 0));
+  store_tile(0);
   __syncthreads();
 
   for (int t = 0; t < rg.n_tiles; ++t) {
     const int buf = t & 1;
     const int kv0 = fwd_tile_kv0<BC, SPARSE>(p, rg, t);
-    if (t + 1 < rg.n_tiles) load_tile(fwd_tile_kv0<BC, SPARSE>(p, rg, t + 1));
+    load_tile(fwd_tile_kv0<BC, SPARSE>(p, rg, min(t + 1, rg.n_tiles - 1)));
 
     // S^T (keys x queries) = K_tile Q^T
     f32x16 sacc[NKB];
@@ -230,12 +225,16 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdKParams p) {
         sacc[kb] = mfma_bf16(a, qf[kk], sacc[kb]);
       }
 
+    const float m_prev = m_run;
     const bool need_mask =
         !SPARSE && ((kv0 + BC > rg.kv_len) || (p.causal && kv0 + BC - 1 > q0 + wave * 32));
     const float alpha = online_softmax_step<NKB>(sacc, need_mask, kv0, rg.kv_len, p.causal, qrow, g,
                                                  p.c, m_run, l_run);
+    // alpha == 1 exactly when no row max of this wave grew: skip the rescale then.
+    if (__builtin_amdgcn_ballot_w64(m_run != m_prev)) {
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+      for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+    }
 
     // P^T as B operands: k-step ks = 2 kb + s covers keys 32 kb + 16 s + {4g..4g+3, 8+4g..8+4g+3},
     // which are exactly registers 8 s .. 8 s + 7 of block kb.
@@ -248,23 +247,22 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdKParams p) {
                                      sacc[kb][8 * s + 3], sacc[kb][8 * s + 4], sacc[kb][8 * s + 5],
                                      sacc[kb][8 * s + 6], sacc[kb][8 * s + 7]);
 
-    // O^T (dims x queries) += V^T P^T; A = V^T rows (dims) with the same key slots.
+    // O^T (dims x queries) += V^T P^T; A = V^T through the transposing LDS read,
+    // whose key slots are the same as those of pb.
 #pragma unroll
     for (int ks = 0; ks < BC / 16; ++ks)
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const bf16* vp = &sVt[buf][(db * 32 + l32) * VP + 16 * ks + 4 * g];
-        const bf16x8 a = concat_bf16x4(*reinterpret_cast<const bf16x4*>(vp),
-                                       *reinterpret_cast<const bf16x4*>(vp + 8));
+        const bf16x8 a = lds_read_tr_k16(sV[buf], VP, 16 * ks, 32 * db, lane);
         oacc[db] = mfma_bf16(a, pb[ks], oacc[db]);
       }
 
-    if (t + 1 < rg.n_tiles) store_tile(buf ^ 1);
+    store_tile(buf ^ 1);
     __syncthreads();
   }
 
   // Epilogue: O = O_acc / l, LSE = (m + log2 l) ln 2. Rows with no key: O = 0, LSE = -inf.
-  const float l_tot = l_run + other_half(l_run);
+  const float l_tot = pair_sum(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (qrow < N) {
     bf16* Orow = static_cast<bf16*>(p.o) + base + (int64_t)qrow * p.sn;
@@ -380,7 +378,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdKParams p) {
     __syncthreads();
   }
 
-  const float l_tot = l_run + other_half(l_run);
+  const float l_tot = pair_sum(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (qrow < N) {
     float* Orow = static_cast<float*>(p.o) + base + (int64_t)qrow * p.sn;

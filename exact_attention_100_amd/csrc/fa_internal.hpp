@@ -40,10 +40,12 @@ struct BwdArgs {
   int causal;
   const int32_t* key_len;
   // workspace sections
-  float* dq_acc;  // [B, H, N, d] float32
   float* delta;   // [B, H, N]: rowsum(dO o O)
   float* lse2;    // [B, H, N]: LSE * log2(e) (+inf for rows with no key)
-  // Block-sparse (col_ptr != nullptr): CSC lists of kept query blocks per key block.
+  // Block-sparse (col_ptr != nullptr): CSR lists of kept key blocks per query
+  // block and CSC lists of kept query blocks per key block.
+  const int32_t* row_ptr;
+  const int32_t* col_idx;
   const int32_t* col_ptr;
   const int32_t* row_idx;
   int block_size;

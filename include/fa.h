@@ -81,9 +81,9 @@ typedef struct fa_desc {
 int fa_fwd(const fa_desc* desc, const void* Q, const void* K, const void* V, float scale,
            int causal, const int32_t* key_len, void* O, float* LSE, void* stream);
 
-/* Bytes of device workspace fa_bwd needs: a float32 dQ accumulator and one
- * float32 per row, i.e. O(N d) per head and never O(N^2) (the linear extra
- * memory of Theorem 1, anthology LIT-074 key takeaways). */
+/* Bytes of device workspace fa_bwd needs: two float32 values per row
+ * (rowsum(dO o O) and the base-2 LSE), i.e. O(N) per head and never O(N^2)
+ * (the linear extra memory of Theorem 1, anthology LIT-074 key takeaways). */
 size_t fa_bwd_workspace_bytes(const fa_desc* desc);
 
 /* Backward: the gradient of <dO, O> with respect to Q, K and V, given the O and
