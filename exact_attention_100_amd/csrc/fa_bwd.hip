@@ -89,9 +89,12 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdKParams p) {
 
 // ------------------------------------------------------------------------------ dK, dV
 
-// Query rows per tile of the dK/dV pass.
-#ifndef FA_BWD_TILE_Q
-#define FA_BWD_TILE_Q 32
+// Query rows per tile of the dK/dV pass, per head dim.
+#ifndef FA_BWD_TILE_Q_D128
+#define FA_BWD_TILE_Q_D128 32
+#endif
+#ifndef FA_BWD_TILE_Q_D64
+#define FA_BWD_TILE_Q_D64 64
 #endif
 
 // Per query tile of BRQ rows (double-buffered in LDS by direct copies, one
@@ -174,17 +177,22 @@ void bwd_dkdv_kernel(BwdKParams p) {
     const int64_t koff = (int64_t)min(mykey, N - 1) * p.sn + 8 * g;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) kf[kk] = *reinterpret_cast<const bf16x8*>(Kh + koff + 16 * kk);
+    const int wu = uniform_wave_id();
     if constexpr (VLDS) {
       // keys past the end are clamped (their P is 0)
-      tile_dma<kBwdBlock, D, 4>(sV, Vh, p.sn, k0, N, wave, lane);
+      TileCopy<kBwdBlock, D, 4> cpv;
+      cpv.init(wu, lane);
+      cpv.issue(sV, Vh, p.sn, k0, N);
     } else {
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) vf[kk] = *reinterpret_cast<const bf16x8*>(Vh + koff + 16 * kk);
     }
 
+    TileCopy<BRQ, D, 4> cp;
+    cp.init(wu, lane);
     auto issue_tile = [&](int q0, int buf) {
-      tile_dma<BRQ, D, 4>(sQ[buf], Qh, p.sn, q0, N, wave, lane);
-      tile_dma<BRQ, D, 4>(sdO[buf], dOh, p.sn, q0, N, wave, lane);
+      cp.issue(sQ[buf], Qh, p.sn, q0, N);
+      cp.issue(sdO[buf], dOh, p.sn, q0, N);
       if (wave == 0) vec_dma64(sL[buf], p.lse2 + rowbase, q0, N, lane);
       if (wave == 1) vec_dma64(sDl[buf], p.delta + rowbase, q0, N, lane);
     };
@@ -229,6 +237,8 @@ void bwd_dkdv_kernel(BwdKParams p) {
       // only when they exist in the loaded statistics, so they are masked too.
       const bool need_mask =
           !SPARSE && ((p.causal && q0 < kw0 + 31) || (kw0 + 32 > kv_len) || (q0 + BRQ > N));
+      // (one code path: this kernel is bound by the MFMA pipe, and a second,
+      // mask-free copy of this block would push d = 128 past 256 registers)
 #pragma unroll
       for (int sb = 0; sb < NQB; ++sb)
 #pragma unroll
@@ -383,9 +393,11 @@ void bwd_dq_kernel(BwdKParams p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) dqacc[db][r] = 0.f;
 
+  TileCopy<BC, D, 4> cp;
+  cp.init(uniform_wave_id(), lane);
   auto issue_tile = [&](int kv0, int buf) {
-    tile_dma<BC, D, 4>(sK[buf], Kh, p.sn, kv0, N, wave, lane);
-    tile_dma<BC, D, 4>(sV[buf], Vh, p.sn, kv0, N, wave, lane);
+    cp.issue(sK[buf], Kh, p.sn, kv0, N);
+    cp.issue(sV[buf], Vh, p.sn, kv0, N);
   };
   issue_tile(tile_kv0(0), 0);
   wait_vmem();
@@ -416,19 +428,25 @@ void bwd_dq_kernel(BwdKParams p) {
 
     // dS^T = P^T (dP^T - D); register r of block kb is key kv0 + 32 kb + 8 (r/4) + 4 g + r%4.
     const bool need_mask = !SPARSE && ((kv0 + BC > kv_len) || (p.causal && kv0 + BC - 1 > q0 + 32 * wave));
+    auto ds = [&](auto masked) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float pr = fast_exp2(fmaf(sacc[kb][r], p.c, -lse2_q));
+          if constexpr (decltype(masked)::value) {
+            const int key = kv0 + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
+            const bool ok = key < kv_len && (!p.causal || key <= qrow);
+            if (!ok) pr = 0.f;
+          }
+          dpacc[kb][r] = pr * (dpacc[kb][r] - d_q);
+        }
+    };
+    if (need_mask) ds(Flag<true>());
+    else ds(Flag<false>());
     bf16x8 dsb[2 * NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float pr = fast_exp2(fmaf(sacc[kb][r], p.c, -lse2_q));
-        if (need_mask) {
-          const int key = kv0 + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
-          const bool ok = key < kv_len && (!p.causal || key <= qrow);
-          if (!ok) pr = 0.f;
-        }
-        dpacc[kb][r] = pr * (dpacc[kb][r] - d_q);
-      }
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         const f32x16& S = dpacc[kb];
@@ -508,15 +526,16 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
-  constexpr int TQ = FA_BWD_TILE_Q, TK128 = FA_BWD_TILE_K_D128, TK64 = FA_BWD_TILE_K_D64;
+  constexpr int TQ128 = FA_BWD_TILE_Q_D128, TQ64 = FA_BWD_TILE_Q_D64;
+  constexpr int TK128 = FA_BWD_TILE_K_D128, TK64 = FA_BWD_TILE_K_D64;
   const dim3 grid((unsigned)(a.B * a.H * p.n_blocks));
   timer_begin("fa_bwd_dkdv", s);
   if (a.d == 128) {
-    if (sparse) bwd_dkdv_kernel<128, TQ, true, true><<<grid, block, 0, s>>>(p);
-    else bwd_dkdv_kernel<128, TQ, false, true><<<grid, block, 0, s>>>(p);
+    if (sparse) bwd_dkdv_kernel<128, TQ128, true, true><<<grid, block, 0, s>>>(p);
+    else bwd_dkdv_kernel<128, TQ128, false, true><<<grid, block, 0, s>>>(p);
   } else {
-    if (sparse) bwd_dkdv_kernel<64, TQ, true, false><<<grid, block, 0, s>>>(p);
-    else bwd_dkdv_kernel<64, TQ, false, false><<<grid, block, 0, s>>>(p);
+    if (sparse) bwd_dkdv_kernel<64, TQ64, true, false><<<grid, block, 0, s>>>(p);
+    else bwd_dkdv_kernel<64, TQ64, false, false><<<grid, block, 0, s>>>(p);
   }
   timer_end(s);
   e = hipGetLastError();

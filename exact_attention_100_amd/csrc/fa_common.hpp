@@ -145,28 +145,59 @@ __device__ __forceinline__ bf16x8 lds_read_tr_k16_swz(const bf16* X, int k0, int
   return concat_bf16x4(lo, hi);
 }
 
-// Direct global -> LDS copy of a [ROWS x COLS] bf16 tile into the swizzled
+// Direct global -> LDS copies of a [ROWS x COLS] bf16 tile into the swizzled
 // layout above (global_load_lds_dwordx4: lane i of an instruction writes LDS
 // chunk base + i, so each lane fetches the global chunk that belongs there).
-// Global rows row0 + r past nvalid are clamped to row nvalid - 1 (see the
-// callers for why the clamped values are harmless). NWAVES waves share the
-// copy; the caller waits (vmcnt) and synchronises before the tile is read.
+// The per-lane source offsets are computed once (init); issue() then costs one
+// address add per copy for a full tile. Rows row0 + r at or past nvalid are
+// clamped to row nvalid - 1 (the callers only ever give such rows probability
+// 0 or discard what they produce). NWAVES waves share a copy; the caller waits
+// (vmcnt) and synchronises before the tile is read.
 template <int ROWS, int COLS, int NWAVES>
-__device__ __forceinline__ void tile_dma(bf16* lds_tile, const bf16* g, int64_t ld, int row0, int nvalid,
-                                         int wave, int lane) {
-  constexpr int CPR = COLS / 8;
-  constexpr int PER_WAVE = ROWS * CPR / (64 * NWAVES);
+struct TileCopy {
+  static constexpr int CPR = COLS / 8;
+  static constexpr int PER_WAVE = ROWS * CPR / (64 * NWAVES);
   static_assert(PER_WAVE >= 1 && PER_WAVE * 64 * NWAVES == ROWS * CPR, "tile must split into whole wave copies");
+  int32_t row[PER_WAVE];  // tile row of this lane's chunk in copy i
+  int32_t col[PER_WAVE];  // element column of that chunk in global memory
+  int wave;               // wave index (uniform)
+
+  __device__ __forceinline__ void init(int wave_uniform, int lane) {
+    wave = wave_uniform;
 #pragma unroll
-  for (int i = 0; i < PER_WAVE; ++i) {
-    const int base = (i * NWAVES + wave) * 64;  // first LDS chunk of this copy (wave-uniform)
-    const int pch = base + lane;
-    const int r = pch / CPR, lc = (pch % CPR) ^ tile_swz<COLS>(r);
-    const int64_t grow = min(row0 + r, nvalid - 1);
-    __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(g + grow * ld + 8 * lc),
-                                     (void __attribute__((address_space(3)))*)(lds_tile + 8 * base), 16, 0, 0);
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const int pch = (i * NWAVES + wave) * 64 + lane;
+      row[i] = pch / CPR;
+      col[i] = 8 * ((pch % CPR) ^ tile_swz<COLS>(row[i]));
+    }
   }
-}
+  __device__ __forceinline__ void issue(bf16* lds_tile, const bf16* g, int64_t ld, int row0, int nvalid) const {
+    typedef const void __attribute__((address_space(1)))* gptr;
+    typedef void __attribute__((address_space(3)))* lptr;
+    if (row0 + ROWS <= nvalid) {
+      const bf16* gt = g + (int64_t)row0 * ld;
+#pragma unroll
+      for (int i = 0; i < PER_WAVE; ++i)
+        __builtin_amdgcn_global_load_lds((gptr)(gt + (int64_t)row[i] * ld + col[i]),
+                                         (lptr)(lds_tile + 8 * 64 * (i * NWAVES + wave)), 16, 0, 0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < PER_WAVE; ++i)
+        __builtin_amdgcn_global_load_lds((gptr)(g + (int64_t)min(row0 + row[i], nvalid - 1) * ld + col[i]),
+                                         (lptr)(lds_tile + 8 * 64 * (i * NWAVES + wave)), 16, 0, 0);
+    }
+  }
+};
+
+// Compile-time flag for generic lambdas (selects the masked / unmasked variant
+// of a tile body without per-element branches).
+template <bool B>
+struct Flag {
+  static constexpr bool value = B;
+};
+
+// Wave index as a wave-uniform (scalar) value.
+__device__ __forceinline__ int uniform_wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 // Same for a vector of COUNT (<= 64) floats: one copy by one wave; lanes past
 // COUNT write the padding of a 64-float LDS array.

@@ -10,9 +10,10 @@
 // section states.
 //
 // gfx950 mapping (our design):
-//   * 4 waves x 32 query rows = 128 rows per workgroup; K/V tiles of BC keys,
-//     double-buffered row-major in LDS; the V^T operand of P V comes from the
-//     transposing LDS read (ds_read_b64_tr_b16), two per MFMA.
+//   * 4 waves x 32 query rows = 128 rows per workgroup; K/V tiles of BC keys
+//     arrive by direct global -> LDS copies, double-buffered, row-major in a
+//     swizzled layout; the V^T operand of P V comes from the transposing LDS
+//     read (ds_read_b64_tr_b16), two per MFMA.
 //   * Each wave computes S^T = K Q^T on the 32x32x16 bf16 MFMA, so a lane owns
 //     ONE query column and 16 keys of it: row max / row sum are per-lane
 //     reductions plus one exchange with lane l^32, the rescale factor is one
@@ -85,11 +86,10 @@ __device__ __forceinline__ int fwd_tile_kv0(const FwdKParams& p, const FwdRange&
 // 4 g + r%4). Masked entries become probability 0. On return s[] holds the
 // unnormalised probabilities 2^(c S - m) and alpha the factor that rescales
 // everything accumulated before this tile.
-template <int NKB>
-__device__ __forceinline__ float online_softmax_step(f32x16 (&s)[NKB], bool need_mask, int kv0,
-                                                     int kv_len, int causal, int qrow, int g,
-                                                     float c, float& m_run, float& l_run) {
-  if (need_mask) {
+template <int NKB, bool MASKED>
+__device__ __forceinline__ float online_softmax_step(f32x16 (&s)[NKB], int kv0, int kv_len, int causal,
+                                                     int qrow, int g, float c, float& m_run, float& l_run) {
+  if (MASKED) {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -116,7 +116,7 @@ __device__ __forceinline__ float online_softmax_step(f32x16 (&s)[NKB], bool need
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       float pv = fast_exp2(fmaf(s[kb][r], c, -m_use));
-      if (need_mask && s[kb][r] == kNegInf) pv = 0.f;
+      if (MASKED && s[kb][r] == kNegInf) pv = 0.f;  // exact 0 also when c = 0
       s[kb][r] = pv;
       rs += pv;
     }
@@ -135,16 +135,15 @@ __device__ __forceinline__ float online_softmax_step(f32x16 (&s)[NKB], bool need
 template <int D, int BC, bool SPARSE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FA_FWD_WAVES_PER_EU)))
 void fwd_bf16_kernel(FwdKParams p) {
-  constexpr int KP = D + 8;   // K tile row stride: 16-byte rows spread over the banks
-  constexpr int VP = D + 32;  // V tile row stride: the 4 rows of a transposing read hit disjoint banks
   constexpr int NKB = BC / 32;
   constexpr int NDB = D / 32;
   constexpr int NKK = D / 16;
-  constexpr int CHUNKS = BC * D / 8 / 256;  // 16-byte chunks of K (and of V) per thread per tile
-  static_assert(CHUNKS >= 1, "tile too small for 256 threads");
+  constexpr int TILE = BC * D;
 
-  __shared__ __attribute__((aligned(16))) bf16 sK[2][BC * KP];
-  __shared__ __attribute__((aligned(16))) bf16 sV[2][BC * VP];
+  // K and V tiles, double-buffered, row-major in the swizzled layout (16-byte
+  // row reads for the K operand, transposing reads for the V^T operand).
+  __shared__ __attribute__((aligned(16))) bf16 sK[2][TILE];
+  __shared__ __attribute__((aligned(16))) bf16 sV[2][TILE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5;
@@ -161,37 +160,15 @@ void fwd_bf16_kernel(FwdKParams p) {
   const int qrow = q0 + wave * 32 + l32;
   const FwdRange rg = fwd_range<BC, SPARSE>(p, b, q0);
 
+  // Every global load is unconditional: rows past the end are clamped to row
+  // N - 1, whose values then only ever meet probability 0 (masked keys) or feed
+  // outputs that are not stored (query rows >= N).
   // This lane's query, as the B operand of S^T = K Q^T: slot group g of k-step
   // kk holds dims [16 kk + 8 g, 16 kk + 8 g + 8).
-  // Every global load below is unconditional: row indices past the end are
-  // clamped to row N - 1, whose values then only ever meet probability 0 (masked
-  // keys) or feed outputs that are not stored (query rows >= N). Branch-free
-  // loads let the compiler count outstanding loads exactly, so prefetches stay
-  // in flight across the MFMA work.
   bf16x8 qf[NKK];
   const int64_t qoff = (int64_t)min(qrow, N - 1) * p.sn;
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(Qh + qoff + 16 * kk + 8 * g);
-
-  // K and V tiles are staged row-major: 16-byte chunks, D/8 chunks per key.
-  u32x4 kreg[CHUNKS], vreg[CHUNKS];
-  auto load_tile = [&](int kv0) {
-#pragma unroll
-    for (int i = 0; i < CHUNKS; ++i) {
-      const int ci = tid + 256 * i, r = ci / (D / 8), cc = ci - r * (D / 8);
-      const int64_t off = (int64_t)min(kv0 + r, N - 1) * p.sn + 8 * cc;
-      kreg[i] = *reinterpret_cast<const u32x4*>(Kh + off);
-      vreg[i] = *reinterpret_cast<const u32x4*>(Vh + off);
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < CHUNKS; ++i) {
-      const int ci = tid + 256 * i, r = ci / (D / 8), cc = ci - r * (D / 8);
-      *reinterpret_cast<u32x4*>(&sK[buf][r * KP + 8 * cc]) = kreg[i];
-      *reinterpret_cast<u32x4*>(&sV[buf][r * VP + 8 * cc]) = vreg[i];
-    }
-  };
 
   f32x16 oacc[NDB];
 #pragma unroll
@@ -200,16 +177,22 @@ void fwd_bf16_kernel(FwdKParams p) {
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
   float m_run = kNegInf, l_run = 0.f;
 
-  // The tile loop always prefetches (the last iteration re-reads its own tile
-  // into the idle buffer) so that it has no branches around memory operations.
-  load_tile(fwd_tile_kv0<BC, SPARSE>(p, rg, 0));
-  store_tile(0);
+  // Tiles arrive by direct global -> LDS copies; the loop always prefetches (the
+  // last iteration re-reads its own tile into the idle buffer).
+  TileCopy<BC, D, 4> cp;
+  cp.init(uniform_wave_id(), lane);
+  auto issue_tile = [&](int kv0, int buf) {
+    cp.issue(sK[buf], Kh, p.sn, kv0, N);
+    cp.issue(sV[buf], Vh, p.sn, kv0, N);
+  };
+  issue_tile(fwd_tile_kv0<BC, SPARSE>(p, rg, 0), 0);
+  wait_vmem();
   __syncthreads();
 
   for (int t = 0; t < rg.n_tiles; ++t) {
     const int buf = t & 1;
     const int kv0 = fwd_tile_kv0<BC, SPARSE>(p, rg, t);
-    load_tile(fwd_tile_kv0<BC, SPARSE>(p, rg, min(t + 1, rg.n_tiles - 1)));
+    issue_tile(fwd_tile_kv0<BC, SPARSE>(p, rg, min(t + 1, rg.n_tiles - 1)), buf ^ 1);
 
     // S^T (keys x queries) = K_tile Q^T
     f32x16 sacc[NKB];
@@ -221,15 +204,16 @@ void fwd_bf16_kernel(FwdKParams p) {
     for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sK[buf][(kb * 32 + l32) * KP + 16 * kk + 8 * g]);
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sK[buf][tile_off<D>(kb * 32 + l32, 16 * kk + 8 * g)]);
         sacc[kb] = mfma_bf16(a, qf[kk], sacc[kb]);
       }
 
     const float m_prev = m_run;
     const bool need_mask =
         !SPARSE && ((kv0 + BC > rg.kv_len) || (p.causal && kv0 + BC - 1 > q0 + wave * 32));
-    const float alpha = online_softmax_step<NKB>(sacc, need_mask, kv0, rg.kv_len, p.causal, qrow, g,
-                                                 p.c, m_run, l_run);
+    const float alpha =
+        need_mask ? online_softmax_step<NKB, true>(sacc, kv0, rg.kv_len, p.causal, qrow, g, p.c, m_run, l_run)
+                  : online_softmax_step<NKB, false>(sacc, kv0, rg.kv_len, p.causal, qrow, g, p.c, m_run, l_run);
     // alpha == 1 exactly when no row max of this wave grew: skip the rescale then.
     if (__builtin_amdgcn_ballot_w64(m_run != m_prev)) {
 #pragma unroll
@@ -253,11 +237,11 @@ void fwd_bf16_kernel(FwdKParams p) {
     for (int ks = 0; ks < BC / 16; ++ks)
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const bf16x8 a = lds_read_tr_k16(sV[buf], VP, 16 * ks, 32 * db, lane);
+        const bf16x8 a = lds_read_tr_k16_swz<D>(sV[buf], 16 * ks, 32 * db, lane);
         oacc[db] = mfma_bf16(a, pb[ks], oacc[db]);
       }
 
-    store_tile(buf ^ 1);
+    wait_vmem();
     __syncthreads();
   }
 
@@ -360,8 +344,9 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdKParams p) {
     for (int kk = 0; kk < D / 2; ++kk) sacc[0] = mfma_f32(sK[buf][l32 * KP + 2 * kk + g], qf[kk], sacc[0]);
 
     const bool need_mask = (kv0 + BC > rg.kv_len) || (p.causal && kv0 + BC - 1 > q0 + wave * 32);
-    const float alpha = online_softmax_step<1>(sacc, need_mask, kv0, rg.kv_len, p.causal, qrow, g, p.c,
-                                               m_run, l_run);
+    const float alpha =
+        need_mask ? online_softmax_step<1, true>(sacc, kv0, rg.kv_len, p.causal, qrow, g, p.c, m_run, l_run)
+                  : online_softmax_step<1, false>(sacc, kv0, rg.kv_len, p.causal, qrow, g, p.c, m_run, l_run);
 #pragma unroll
     for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
 
@@ -423,17 +408,30 @@ static FwdKParams make_params(const FwdArgs& a) {
   return p;
 }
 
+// Keys per K/V tile of the bf16 forward, per head dim.
+#ifndef FA_FWD_BC_D128
+#define FA_FWD_BC_D128 64
+#endif
+#ifndef FA_FWD_BC_D64
+#define FA_FWD_BC_D64 64
+#endif
+// Block-sparse d = 64: one 128-key tile per 128-key block (no masked tiles there).
+#ifndef FA_FWD_BC_SPARSE_D64
+#define FA_FWD_BC_SPARSE_D64 128
+#endif
+
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s) {
   const FwdKParams p = make_params(a);
   const dim3 grid((unsigned)(a.B * a.H * p.n_qblocks)), block(256);
   const bool sparse = a.row_ptr != nullptr;
   timer_begin("fa_fwd_bf16", s);
+  constexpr int BC128 = FA_FWD_BC_D128, BC64 = FA_FWD_BC_D64, BCS64 = FA_FWD_BC_SPARSE_D64;
   if (a.d == 128) {
-    if (sparse) fwd_bf16_kernel<128, 64, true><<<grid, block, 0, s>>>(p);
-    else fwd_bf16_kernel<128, 64, false><<<grid, block, 0, s>>>(p);
+    if (sparse) fwd_bf16_kernel<128, BC128, true><<<grid, block, 0, s>>>(p);
+    else fwd_bf16_kernel<128, BC128, false><<<grid, block, 0, s>>>(p);
   } else {
-    if (sparse) fwd_bf16_kernel<64, 64, true><<<grid, block, 0, s>>>(p);
-    else fwd_bf16_kernel<64, 64, false><<<grid, block, 0, s>>>(p);
+    if (sparse) fwd_bf16_kernel<64, BCS64, true><<<grid, block, 0, s>>>(p);
+    else fwd_bf16_kernel<64, BC64, false><<<grid, block, 0, s>>>(p);
   }
   timer_end(s);
   return hipGetLastError();
