@@ -58,15 +58,80 @@ def sources_hash() -> str:
 
 def traffic_for(kernel: str, workload: str):
     """HBM bytes per launch measured by rocprofv3 counters, if taken on the current sources."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    path = os.path.join(ROOT, "profiles", f"attention_kernels_{workload}_hbm_traffic.txt")
     if not os.path.exists(path):
         return None
     with open(path) as fh:
-        rec = json.load(fh)
+        text = fh.read()
+    rec = json.loads(text[text.index("{"):])  # the JSON follows a short header
     if rec.get("sources_hash") != sources_hash():
         return None
     k = rec.get("kernels", {}).get(kernel)
     return None if k is None else k.get("hbm_bytes_per_launch")
+
+
+# Library timer names of the kernels, by a fragment of their symbol.
+KERNEL_NAMES = {"fwd_bf16_kernel": "fa_fwd_bf16", "fwd_f32_kernel": "fa_fwd_f32", "bwd_prep_kernel": "fa_bwd_prep",
+                "bwd_dkdv_kernel": "fa_bwd_dkdv", "bwd_dq_kernel": "fa_bwd_dq", "block_lists_kernel": "fa_block_lists"}
+
+
+def calibrate_copy(nbytes: int = 1 << 30, launches: int = 3):
+    """A plain device-to-device copy of known size, run under rocprofv3 --pmc to scale
+    FETCH_SIZE / WRITE_SIZE into bytes."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(launches):
+        torch.mul(src, 1.0, out=dst)  # one elementwise kernel: reads and writes nbytes
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "launches": launches}), flush=True)
+
+
+def _counter_means(d: str, counter: str):
+    """Mean counter value per dispatch, by kernel symbol, from a rocprofv3 --output-format csv run."""
+    import csv
+    import glob
+    vals = {}
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for row in csv.DictReader(fh):
+                if row["Counter_Name"] != counter:
+                    continue
+                vals.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in vals.items()}
+
+
+def digest_counters(fetch_dir: str, write_dir: str, copy_fetch_dir: str, copy_write_dir: str, workload: str):
+    """Per-kernel HBM bytes per launch from FETCH_SIZE / WRITE_SIZE (KiB) runs, each scaled by what the
+    counter reads for the calibration copy of known size. Prints the JSON that bench.py reads."""
+    import workloads
+    case = workloads.make_config(workload)
+    cf, cw = _counter_means(copy_fetch_dir, "FETCH_SIZE"), _counter_means(copy_write_dir, "WRITE_SIZE")
+    # the calibration copy is the dispatch with the largest traffic in its run
+    copy_bytes = 1 << 30
+    kf = copy_bytes / (max(cf.values()) * 1024.0)
+    kw = copy_bytes / (max(cw.values()) * 1024.0)
+    fetch, write = _counter_means(fetch_dir, "FETCH_SIZE"), _counter_means(write_dir, "WRITE_SIZE")
+    e = 2
+    B, H, N, d = case.B, case.H, case.N, case.d
+    rows = B * H * N
+    algo = {"fa_fwd_bf16": 4 * rows * d * e + 4 * rows, "fa_bwd_dkdv": 6 * rows * d * e + 8 * rows,
+            "fa_bwd_dq": 5 * rows * d * e + 8 * rows, "fa_bwd_prep": 2 * rows * d * e + 12 * rows}
+    kernels = {}
+    for sym, kib in fetch.items():
+        name = next((v for k, v in KERNEL_NAMES.items() if k in sym), None)
+        if name is None:
+            continue
+        wkib = next((w for s2, w in write.items() if s2 == sym), 0.0)
+        rd, wr = kib * 1024.0 * kf, wkib * 1024.0 * kw
+        kernels[name] = {"symbol": sym, "fetch_kib": round(kib, 1), "write_kib": round(wkib, 1),
+                         "hbm_read_bytes": round(rd), "hbm_write_bytes": round(wr),
+                         "hbm_bytes_per_launch": round(rd + wr), "algorithmic_bytes": algo.get(name),
+                         "ratio_to_algorithmic": round((rd + wr) / algo[name], 3) if name in algo else None}
+    out = {"workload": workload, "sources_hash": sources_hash(),
+           "calibration": {"copy_bytes": copy_bytes, "fetch_scale": round(kf, 4), "write_scale": round(kw, 4)},
+           "kernels": kernels}
+    print(json.dumps(out, indent=1), flush=True)
 
 
 def cpu_baseline(case, budget_s: float):
@@ -105,7 +170,17 @@ def main():
     ap.add_argument("--workload", default="C4b")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true", help="only run a 1 GiB device copy (counter scale)")
+    ap.add_argument("--digest-counters", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
+                                                           "COPY_WRITE_DIR"),
+                    help="print per-kernel HBM traffic from rocprofv3 --pmc csv runs")
     args = ap.parse_args()
+    if args.digest_counters:
+        digest_counters(*args.digest_counters, workload=args.workload)
+        return
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not supported",
               file=sys.stderr, flush=True)

@@ -9,9 +9,10 @@ What it computes, per (batch, head) instance with Q, K, V in R^{N x d}:
   -- FlashAttention reading notes (hackmd), §Background › Standard Attention
   Implementation, the S / P / O equations. The pages write S = Q K^T; the
   caller's scale multiplies S (a reading: the workloads use 1/sqrt(d)).
-Masking sets disallowed entries of S to -inf before the softmax (the fused
-kernel there runs "matmul, softmax, masking/dropout, matmul"; the order is read
-as mask-before-softmax so that masked keys get zero probability):
+Masking sets disallowed entries of S to -inf before the softmax (the notes'
+description of the fused kernel lists masking next to dropout after the
+softmax; it is read as mask-before-softmax so that masked keys get zero
+probability):
   * causal: key j is allowed for query i iff j <= i;
   * key padding: keys j >= key_len[b] are masked for every query of batch b;
   * block-sparse: entry (i, j) is allowed iff block_mask[i // bs, j // bs] != 0
