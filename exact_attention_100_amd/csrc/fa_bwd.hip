@@ -181,7 +181,7 @@ void bwd_dkdv_kernel(BwdKParams p) {
     if constexpr (VLDS) {
       // keys past the end are clamped (their P is 0)
       TileCopy<kBwdBlock, D, 4> cpv;
-      cpv.init(wu, lane);
+      cpv.init(wu, lane, p.sn);
       cpv.issue(sV, Vh, p.sn, k0, N);
     } else {
 #pragma unroll
@@ -189,7 +189,9 @@ void bwd_dkdv_kernel(BwdKParams p) {
     }
 
     TileCopy<BRQ, D, 4> cp;
-    cp.init(wu, lane);
+    cp.init(wu, lane, p.sn);
+    TileOffsets<D> to;
+    to.init(lane);
     auto issue_tile = [&](int q0, int buf) {
       cp.issue(sQ[buf], Qh, p.sn, q0, N);
       cp.issue(sdO[buf], dOh, p.sn, q0, N);
@@ -222,14 +224,13 @@ void bwd_dkdv_kernel(BwdKParams p) {
       for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
         for (int sb = 0; sb < NQB; ++sb) {
-          const int off = tile_off<D>(32 * sb + l32, 16 * kk + 8 * g);
           bf16x8 vb;
           if constexpr (VLDS)
-            vb = *reinterpret_cast<const bf16x8*>(&sV[tile_off<D>(32 * wave + l32, 16 * kk + 8 * g)]);
+            vb = to.read_row(sV, wu, kk);
           else
             vb = vf[kk];
-          sacc[sb] = mfma_bf16(*reinterpret_cast<const bf16x8*>(&sQ[cur][off]), kf[kk], sacc[sb]);
-          dpacc[sb] = mfma_bf16(*reinterpret_cast<const bf16x8*>(&sdO[cur][off]), vb, dpacc[sb]);
+          sacc[sb] = mfma_bf16(to.read_row(sQ[cur], sb, kk), kf[kk], sacc[sb]);
+          dpacc[sb] = mfma_bf16(to.read_row(sdO[cur], sb, kk), vb, dpacc[sb]);
         }
 
       // P = 2^(c S - lse2), dS = P (dP - D). Register r of sub-block sb is query
@@ -237,8 +238,17 @@ void bwd_dkdv_kernel(BwdKParams p) {
       // only when they exist in the loaded statistics, so they are masked too.
       const bool need_mask =
           !SPARSE && ((p.causal && q0 < kw0 + 31) || (kw0 + 32 > kv_len) || (q0 + BRQ > N));
-      // (one code path: this kernel is bound by the MFMA pipe, and a second,
-      // mask-free copy of this block would push d = 128 past 256 registers)
+      // Masked entries of S become -inf, so that 2^(c S - lse2) = 0 there (c > 0).
+      if (need_mask) {
+#pragma unroll
+        for (int sb = 0; sb < NQB; ++sb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int qi = q0 + 32 * sb + 8 * (r >> 2) + 4 * g + (r & 3);
+            const bool ok = mykey < kv_len && qi < N && (!p.causal || mykey <= qi);
+            if (!ok) sacc[sb][r] = kNegInf;
+          }
+      }
 #pragma unroll
       for (int sb = 0; sb < NQB; ++sb)
 #pragma unroll
@@ -248,12 +258,7 @@ void bwd_dkdv_kernel(BwdKParams p) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int r = 4 * j + i;
-            float pr = fast_exp2(fmaf(sacc[sb][r], p.c, -lv[i]));
-            if (need_mask) {
-              const int qi = q0 + 32 * sb + 8 * j + 4 * g + i;
-              const bool ok = mykey < kv_len && qi < N && (!p.causal || mykey <= qi);
-              if (!ok) pr = 0.f;
-            }
+            const float pr = fast_exp2(fmaf(sacc[sb][r], p.c, -lv[i]));
             sacc[sb][r] = pr;
             dpacc[sb][r] = pr * (dpacc[sb][r] - dv[i]);
           }
@@ -280,8 +285,8 @@ void bwd_dkdv_kernel(BwdKParams p) {
       for (int qs = 0; qs < 2 * NQB; ++qs)
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          dvacc[db] = mfma_bf16(lds_read_tr_k16_swz<D>(sdO[cur], 16 * qs, 32 * db, lane), pb[qs], dvacc[db]);
-          dkacc[db] = mfma_bf16(lds_read_tr_k16_swz<D>(sQ[cur], 16 * qs, 32 * db, lane), dsb[qs], dkacc[db]);
+          dvacc[db] = mfma_bf16(to.read_tr(sdO[cur], qs, db), pb[qs], dvacc[db]);
+          dkacc[db] = mfma_bf16(to.read_tr(sQ[cur], qs, db), dsb[qs], dkacc[db]);
         }
 
       wait_vmem();
@@ -394,7 +399,9 @@ void bwd_dq_kernel(BwdKParams p) {
     for (int r = 0; r < 16; ++r) dqacc[db][r] = 0.f;
 
   TileCopy<BC, D, 4> cp;
-  cp.init(uniform_wave_id(), lane);
+  cp.init(uniform_wave_id(), lane, p.sn);
+  TileOffsets<D> to;
+  to.init(lane);
   auto issue_tile = [&](int kv0, int buf) {
     cp.issue(sK[buf], Kh, p.sn, kv0, N);
     cp.issue(sV[buf], Vh, p.sn, kv0, N);
@@ -421,29 +428,30 @@ void bwd_dq_kernel(BwdKParams p) {
     for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        const int off = tile_off<D>(32 * kb + l32, 16 * kk + 8 * g);
-        sacc[kb] = mfma_bf16(*reinterpret_cast<const bf16x8*>(&sK[buf][off]), qf[kk], sacc[kb]);
-        dpacc[kb] = mfma_bf16(*reinterpret_cast<const bf16x8*>(&sV[buf][off]), df[kk], dpacc[kb]);
+        sacc[kb] = mfma_bf16(to.read_row(sK[buf], kb, kk), qf[kk], sacc[kb]);
+        dpacc[kb] = mfma_bf16(to.read_row(sV[buf], kb, kk), df[kk], dpacc[kb]);
       }
 
     // dS^T = P^T (dP^T - D); register r of block kb is key kv0 + 32 kb + 8 (r/4) + 4 g + r%4.
     const bool need_mask = !SPARSE && ((kv0 + BC > kv_len) || (p.causal && kv0 + BC - 1 > q0 + 32 * wave));
-    auto ds = [&](auto masked) {
+    // Masked entries of S become -inf, so that 2^(c S - lse2) = 0 there (c > 0).
+    if (need_mask) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float pr = fast_exp2(fmaf(sacc[kb][r], p.c, -lse2_q));
-          if constexpr (decltype(masked)::value) {
-            const int key = kv0 + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
-            const bool ok = key < kv_len && (!p.causal || key <= qrow);
-            if (!ok) pr = 0.f;
-          }
-          dpacc[kb][r] = pr * (dpacc[kb][r] - d_q);
+          const int key = kv0 + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
+          const bool ok = key < kv_len && (!p.causal || key <= qrow);
+          if (!ok) sacc[kb][r] = kNegInf;
         }
-    };
-    if (need_mask) ds(Flag<true>());
-    else ds(Flag<false>());
+    }
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float pr = fast_exp2(fmaf(sacc[kb][r], p.c, -lse2_q));
+        dpacc[kb][r] = pr * (dpacc[kb][r] - d_q);
+      }
     bf16x8 dsb[2 * NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
@@ -461,7 +469,7 @@ void bwd_dq_kernel(BwdKParams p) {
     for (int ks = 0; ks < BC / 16; ++ks)
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
-        dqacc[db] = mfma_bf16(lds_read_tr_k16_swz<D>(sK[buf], 16 * ks, 32 * db, lane), dsb[ks], dqacc[db]);
+        dqacc[db] = mfma_bf16(to.read_tr(sK[buf], ks, db), dsb[ks], dqacc[db]);
 
     wait_vmem();
     __syncthreads();
@@ -504,7 +512,8 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s) {
   p.H = a.H;
   p.N = a.N;
   p.scale = a.scale;
-  p.c = a.scale * kLog2e;
+  // kept positive (see the forward): masked scores (-inf) then always give P = 0
+  p.c = fmaxf(a.scale * kLog2e, 1.17549435e-38f);
   p.causal = a.causal;
   p.key_len = a.key_len;
   p.row_ptr = a.row_ptr;

@@ -158,34 +158,70 @@ struct TileCopy {
   static constexpr int CPR = COLS / 8;
   static constexpr int PER_WAVE = ROWS * CPR / (64 * NWAVES);
   static_assert(PER_WAVE >= 1 && PER_WAVE * 64 * NWAVES == ROWS * CPR, "tile must split into whole wave copies");
-  int32_t row[PER_WAVE];  // tile row of this lane's chunk in copy i
-  int32_t col[PER_WAVE];  // element column of that chunk in global memory
+  int32_t off[PER_WAVE];  // element offset of this lane's source chunk from the tile's first row
+  int32_t row[PER_WAVE];  // tile row of that chunk
   int wave;               // wave index (uniform)
 
-  __device__ __forceinline__ void init(int wave_uniform, int lane) {
+  __device__ __forceinline__ void init(int wave_uniform, int lane, int64_t ld) {
     wave = wave_uniform;
 #pragma unroll
     for (int i = 0; i < PER_WAVE; ++i) {
       const int pch = (i * NWAVES + wave) * 64 + lane;
       row[i] = pch / CPR;
-      col[i] = 8 * ((pch % CPR) ^ tile_swz<COLS>(row[i]));
+      off[i] = (int32_t)(row[i] * ld) + 8 * ((pch % CPR) ^ tile_swz<COLS>(row[i]));
     }
   }
   __device__ __forceinline__ void issue(bf16* lds_tile, const bf16* g, int64_t ld, int row0, int nvalid) const {
     typedef const void __attribute__((address_space(1)))* gptr;
     typedef void __attribute__((address_space(3)))* lptr;
+    const bf16* gt = g + (int64_t)row0 * ld;
     if (row0 + ROWS <= nvalid) {
-      const bf16* gt = g + (int64_t)row0 * ld;
 #pragma unroll
       for (int i = 0; i < PER_WAVE; ++i)
-        __builtin_amdgcn_global_load_lds((gptr)(gt + (int64_t)row[i] * ld + col[i]),
-                                         (lptr)(lds_tile + 8 * 64 * (i * NWAVES + wave)), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((gptr)(gt + off[i]), (lptr)(lds_tile + 8 * 64 * (i * NWAVES + wave)),
+                                         16, 0, 0);
     } else {
 #pragma unroll
-      for (int i = 0; i < PER_WAVE; ++i)
-        __builtin_amdgcn_global_load_lds((gptr)(g + (int64_t)min(row0 + row[i], nvalid - 1) * ld + col[i]),
+      for (int i = 0; i < PER_WAVE; ++i) {
+        const int over = max(row0 + row[i] - (nvalid - 1), 0);  // rows to step back to row nvalid - 1
+        __builtin_amdgcn_global_load_lds((gptr)(gt + off[i] - (int64_t)over * ld),
                                          (lptr)(lds_tile + 8 * 64 * (i * NWAVES + wave)), 16, 0, 0);
+      }
     }
+  }
+};
+
+// Loop-invariant per-lane element offsets into swizzled [rows x COLS] tiles.
+// Row reads: the MFMA A operand of rows 32 b + l32 at k-step kk (16 columns,
+// lane group g taking columns 8 g .. 8 g + 7) lives at b * 32 * COLS + row[kk]
+// (the swizzle depends only on the row's low four bits).
+// Transposing reads (lds_read_tr_k16_swz) at k0 = 16 ks, m0 = 32 mb read
+// 16 ks * COLS + tr_lo[mb] and 16 ks * COLS + tr_hi[mb].
+template <int COLS>
+struct TileOffsets {
+  int32_t row[COLS / 16];
+  int32_t tr_lo[COLS / 32], tr_hi[COLS / 32];
+  __device__ __forceinline__ void init(int lane) {
+    const int l32 = lane & 31, g = lane >> 5, h = (lane >> 4) & 1, j = lane & 15;
+#pragma unroll
+    for (int kk = 0; kk < COLS / 16; ++kk) row[kk] = tile_off<COLS>(l32, 16 * kk + 8 * g);
+    const int r = 4 * g + (j >> 2);
+#pragma unroll
+    for (int mb = 0; mb < COLS / 32; ++mb) {
+      const int c = 32 * mb + 16 * h + 4 * (j & 3);
+      tr_lo[mb] = tile_off<COLS>(r, c);
+      tr_hi[mb] = tile_off<COLS>(r + 8, c);
+    }
+  }
+  __device__ __forceinline__ bf16x8 read_row(const bf16* X, int b, int kk) const {
+    return *reinterpret_cast<const bf16x8*>(X + b * 32 * COLS + row[kk]);
+  }
+  __device__ __forceinline__ bf16x8 read_tr(const bf16* X, int ks, int mb) const {
+    typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+    const bf16* p = X + 16 * ks * COLS;
+    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + tr_lo[mb]));
+    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + tr_hi[mb]));
+    return concat_bf16x4(lo, hi);
   }
 };
 

@@ -44,6 +44,7 @@ struct FwdKParams {
 };
 
 constexpr int kFwdRows = 128;  // query rows per workgroup (4 waves x 32)
+constexpr float kRescaleSlack = 8.f;
 
 // Key range and tile count of one workgroup, shared by the bf16 and f32 kernels.
 struct FwdRange {
@@ -81,24 +82,30 @@ __device__ __forceinline__ int fwd_tile_kv0(const FwdKParams& p, const FwdRange&
   return t * BC;
 }
 
-// One online-softmax step over the S^T registers of a tile (NKB blocks of 32
-// keys; lane = one query, register r of block kb = key kv0 + 32 kb + 8 (r/4) +
-// 4 g + r%4). Masked entries become probability 0. On return s[] holds the
-// unnormalised probabilities 2^(c S - m) and alpha the factor that rescales
-// everything accumulated before this tile.
-template <int NKB, bool MASKED>
-__device__ __forceinline__ float online_softmax_step(f32x16 (&s)[NKB], int kv0, int kv_len, int causal,
-                                                     int qrow, int g, float c, float& m_run, float& l_run) {
-  if (MASKED) {
+// Masks the S^T registers of a tile (NKB blocks of 32 keys; lane = one query,
+// register r of block kb = key kv0 + 32 kb + 8 (r/4) + 4 g + r%4): entries whose
+// key is past kv_len or, when causal, after the query become -inf.
+template <int NKB>
+__device__ __forceinline__ void mask_tile(f32x16 (&s)[NKB], int kv0, int kv_len, int causal, int qrow, int g) {
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+  for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = kv0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-        const bool ok = key < kv_len && (!causal || key <= qrow);
-        if (!ok) s[kb][r] = kNegInf;
-      }
-  }
+    for (int r = 0; r < 16; ++r) {
+      const int key = kv0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+      const bool ok = key < kv_len && (!causal || key <= qrow);
+      if (!ok) s[kb][r] = kNegInf;
+    }
+}
+
+// One online-softmax step over the (masked) S^T registers of a tile. On return
+// s[] holds the unnormalised probabilities 2^(c S - m) (exactly 0 where S = -inf,
+// as c > 0) and the result is the factor that rescales everything accumulated
+// before this tile. The reference point m only moves when the row max exceeds
+// it by more than kRescaleSlack (base 2): softmax is invariant to the shift,
+// the unnormalised probabilities stay <= 2^kRescaleSlack, and most tiles then
+// need no rescale at all.
+template <int NKB>
+__device__ __forceinline__ float online_softmax_step(f32x16 (&s)[NKB], float c, float& m_run, float& l_run) {
   float mx = kNegInf;
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb)
@@ -106,7 +113,7 @@ __device__ __forceinline__ float online_softmax_step(f32x16 (&s)[NKB], int kv0, 
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
   mx = pair_max(mx);
   const float mxs = (mx == kNegInf) ? kNegInf : mx * c;
-  const float m_new = fmaxf(m_run, mxs);
+  const float m_new = (mxs > m_run + kRescaleSlack) ? mxs : m_run;
   const float m_use = (m_new == kNegInf) ? 0.f : m_new;
   const float alpha = fast_exp2(m_run - m_use);
   m_run = m_new;
@@ -115,8 +122,7 @@ __device__ __forceinline__ float online_softmax_step(f32x16 (&s)[NKB], int kv0, 
   for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      float pv = fast_exp2(fmaf(s[kb][r], c, -m_use));
-      if (MASKED && s[kb][r] == kNegInf) pv = 0.f;  // exact 0 also when c = 0
+      const float pv = fast_exp2(fmaf(s[kb][r], c, -m_use));
       s[kb][r] = pv;
       rs += pv;
     }
@@ -177,25 +183,21 @@ void fwd_bf16_kernel(FwdKParams p) {
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
   float m_run = kNegInf, l_run = 0.f;
 
-  // Tiles arrive by direct global -> LDS copies; the loop always prefetches (the
-  // last iteration re-reads its own tile into the idle buffer).
+  // Software pipeline over the key tiles. Iteration t computes S(t) = K_t Q^T,
+  // then the P V product of tile t - 1 interleaved with the softmax of tile t, so
+  // that the softmax's VALU and exp work runs while the MFMA pipe executes
+  // P_{t-1} V_{t-1}. The V tile therefore trails the K tile by one: iteration t
+  // copies K_{t+1} and V_t (direct global -> LDS copies, two buffers each; the
+  // last iterations re-read the last tile so that memory operations are never
+  // predicated).
   TileCopy<BC, D, 4> cp;
-  cp.init(uniform_wave_id(), lane);
-  auto issue_tile = [&](int kv0, int buf) {
-    cp.issue(sK[buf], Kh, p.sn, kv0, N);
-    cp.issue(sV[buf], Vh, p.sn, kv0, N);
-  };
-  issue_tile(fwd_tile_kv0<BC, SPARSE>(p, rg, 0), 0);
-  wait_vmem();
-  __syncthreads();
+  cp.init(uniform_wave_id(), lane, p.sn);
+  TileOffsets<D> to;
+  to.init(lane);
+  const int nt = rg.n_tiles;
+  auto kv0_of = [&](int t) { return fwd_tile_kv0<BC, SPARSE>(p, rg, min(t, nt - 1)); };
 
-  for (int t = 0; t < rg.n_tiles; ++t) {
-    const int buf = t & 1;
-    const int kv0 = fwd_tile_kv0<BC, SPARSE>(p, rg, t);
-    issue_tile(fwd_tile_kv0<BC, SPARSE>(p, rg, min(t + 1, rg.n_tiles - 1)), buf ^ 1);
-
-    // S^T (keys x queries) = K_tile Q^T
-    f32x16 sacc[NKB];
+  auto s_mfma = [&](int buf, f32x16 (&sacc)[NKB]) {  // S^T (keys x queries) = K_tile Q^T
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -203,26 +205,20 @@ void fwd_bf16_kernel(FwdKParams p) {
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sK[buf][tile_off<D>(kb * 32 + l32, 16 * kk + 8 * g)]);
-        sacc[kb] = mfma_bf16(a, qf[kk], sacc[kb]);
-      }
-
-    const float m_prev = m_run;
-    const bool need_mask =
-        !SPARSE && ((kv0 + BC > rg.kv_len) || (p.causal && kv0 + BC - 1 > q0 + wave * 32));
-    const float alpha =
-        need_mask ? online_softmax_step<NKB, true>(sacc, kv0, rg.kv_len, p.causal, qrow, g, p.c, m_run, l_run)
-                  : online_softmax_step<NKB, false>(sacc, kv0, rg.kv_len, p.causal, qrow, g, p.c, m_run, l_run);
-    // alpha == 1 exactly when no row max of this wave grew: skip the rescale then.
-    if (__builtin_amdgcn_ballot_w64(m_run != m_prev)) {
+      for (int kb = 0; kb < NKB; ++kb) sacc[kb] = mfma_bf16(to.read_row(sK[buf], kb, kk), qf[kk], sacc[kb]);
+  };
+  // O^T (dims x queries) += V^T P^T; A = V^T through the transposing LDS read,
+  // whose key slots are the same as those of pb.
+  auto pv_mfma = [&](int buf, const bf16x8 (&pb)[2 * NKB]) {
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
-    }
-
-    // P^T as B operands: k-step ks = 2 kb + s covers keys 32 kb + 16 s + {4g..4g+3, 8+4g..8+4g+3},
-    // which are exactly registers 8 s .. 8 s + 7 of block kb.
-    bf16x8 pb[2 * NKB];
+    for (int ks = 0; ks < BC / 16; ++ks)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) oacc[db] = mfma_bf16(to.read_tr(sV[buf], ks, db), pb[ks], oacc[db]);
+  };
+  // Online softmax of one tile, then P^T packed as B operands: k-step ks = 2 kb + s
+  // covers keys 32 kb + 16 s + {4g..4g+3, 8+4g..8+4g+3}, registers 8 s .. 8 s + 7 of block kb.
+  auto softmax_pack = [&](f32x16 (&sacc)[NKB], bf16x8 (&pb)[2 * NKB]) -> float {
+    const float alpha = online_softmax_step<NKB>(sacc, p.c, m_run, l_run);
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -230,19 +226,59 @@ void fwd_bf16_kernel(FwdKParams p) {
         pb[2 * kb + s] = pack_bf16x8(sacc[kb][8 * s + 0], sacc[kb][8 * s + 1], sacc[kb][8 * s + 2],
                                      sacc[kb][8 * s + 3], sacc[kb][8 * s + 4], sacc[kb][8 * s + 5],
                                      sacc[kb][8 * s + 6], sacc[kb][8 * s + 7]);
+    return alpha;
+  };
+  auto needs_mask = [&](int kv0) {
+    return !SPARSE && ((kv0 + BC > rg.kv_len) || (p.causal && kv0 + BC - 1 > q0 + wave * 32));
+  };
 
-    // O^T (dims x queries) += V^T P^T; A = V^T through the transposing LDS read,
-    // whose key slots are the same as those of pb.
-#pragma unroll
-    for (int ks = 0; ks < BC / 16; ++ks)
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const bf16x8 a = lds_read_tr_k16_swz<D>(sV[buf], 16 * ks, 32 * db, lane);
-        oacc[db] = mfma_bf16(a, pb[ks], oacc[db]);
-      }
-
+  if (nt > 0) {
+    bf16x8 pb[2 * NKB];
+    cp.issue(sK[0], Kh, p.sn, kv0_of(0), N);
     wait_vmem();
     __syncthreads();
+    cp.issue(sK[1], Kh, p.sn, kv0_of(1), N);
+    cp.issue(sV[0], Vh, p.sn, kv0_of(0), N);
+    {
+      f32x16 sacc[NKB];
+      s_mfma(0, sacc);
+      if (needs_mask(kv0_of(0))) mask_tile<NKB>(sacc, kv0_of(0), rg.kv_len, p.causal, qrow, g);
+      softmax_pack(sacc, pb);  // (alpha is irrelevant: nothing has been accumulated yet)
+    }
+    wait_vmem();
+    __syncthreads();
+
+    for (int t = 1; t < nt; ++t) {
+      const int kv0 = kv0_of(t);
+      cp.issue(sK[(t + 1) & 1], Kh, p.sn, kv0_of(t + 1), N);
+      cp.issue(sV[t & 1], Vh, p.sn, kv0, N);
+      f32x16 sacc[NKB];
+      s_mfma(t & 1, sacc);
+      if (needs_mask(kv0)) mask_tile<NKB>(sacc, kv0, rg.kv_len, p.causal, qrow, g);
+      const float m_prev = m_run;
+      bf16x8 pbn[2 * NKB];
+      // The P V of tile t - 1 and the softmax of tile t are independent: the
+      // scheduler is asked to interleave them (per MFMA: its two LDS reads, then
+      // a share of the VALU work).
+      pv_mfma((t - 1) & 1, pb);
+      const float alpha = softmax_pack(sacc, pbn);
+#pragma unroll
+      for (int i = 0; i < NDB * BC / 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS reads
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
+      }
+      // alpha == 1 exactly when no row of this wave moved its reference max.
+      if (__builtin_amdgcn_ballot_w64(m_run != m_prev)) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+      }
+#pragma unroll
+      for (int i = 0; i < 2 * NKB; ++i) pb[i] = pbn[i];
+      wait_vmem();
+      __syncthreads();
+    }
+    pv_mfma((nt - 1) & 1, pb);
   }
 
   // Epilogue: O = O_acc / l, LSE = (m + log2 l) ln 2. Rows with no key: O = 0, LSE = -inf.
@@ -344,9 +380,8 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdKParams p) {
     for (int kk = 0; kk < D / 2; ++kk) sacc[0] = mfma_f32(sK[buf][l32 * KP + 2 * kk + g], qf[kk], sacc[0]);
 
     const bool need_mask = (kv0 + BC > rg.kv_len) || (p.causal && kv0 + BC - 1 > q0 + wave * 32);
-    const float alpha =
-        need_mask ? online_softmax_step<1, true>(sacc, kv0, rg.kv_len, p.causal, qrow, g, p.c, m_run, l_run)
-                  : online_softmax_step<1, false>(sacc, kv0, rg.kv_len, p.causal, qrow, g, p.c, m_run, l_run);
+    if (need_mask) mask_tile<1>(sacc, kv0, rg.kv_len, p.causal, qrow, g);
+    const float alpha = online_softmax_step<1>(sacc, p.c, m_run, l_run);
 #pragma unroll
     for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
 
@@ -398,7 +433,10 @@ static FwdKParams make_params(const FwdArgs& a) {
   p.B = a.B;
   p.H = a.H;
   p.N = a.N;
-  p.c = a.scale * kLog2e;
+  // scale * log2(e), kept positive: with scale = 0 the smallest normal float makes
+  // every 2^(c S - m) round to exactly 1 (uniform weights, as for c = 0) while
+  // masked scores (-inf) still give exactly 0.
+  p.c = fmaxf(a.scale * kLog2e, 1.17549435e-38f);
   p.causal = a.causal;
   p.key_len = a.key_len;
   p.row_ptr = a.row_ptr;
