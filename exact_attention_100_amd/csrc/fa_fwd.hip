@@ -255,19 +255,64 @@ void fwd_bf16_kernel(FwdKParams p) {
       f32x16 sacc[NKB];
       s_mfma(t & 1, sacc);
       if (needs_mask(kv0)) mask_tile<NKB>(sacc, kv0, rg.kv_len, p.causal, qrow, g);
-      const float m_prev = m_run;
+
+      // The P V of tile t - 1 and the softmax of tile t are independent. They are
+      // interleaved by hand, one slice of softmax work per P V MFMA (scheduling
+      // fences keep the slices in place): slices 0-1 the row max, slice 2 the new
+      // reference point, the rest the exponentials, row sums and bf16 packing.
+      // The transposing LDS reads of each MFMA's operand run two slices ahead.
+      constexpr int NPV = NDB * (BC / 16);
+      constexpr int NE = NKB * 16;  // scores per lane
+      constexpr int NEXP = NPV - 3; // slices doing exponentials
+      static_assert(NPV >= 4, "too few MFMAs to interleave");
+      const int vb = (t - 1) & 1;
       bf16x8 pbn[2 * NKB];
-      // The P V of tile t - 1 and the softmax of tile t are independent: the
-      // scheduler is asked to interleave them (per MFMA: its two LDS reads, then
-      // a share of the VALU work).
-      pv_mfma((t - 1) & 1, pb);
-      const float alpha = softmax_pack(sacc, pbn);
+      bf16x8 a0 = to.read_tr(sV[vb], 0, 0);
+      bf16x8 a1 = to.read_tr(sV[vb], 1 / NDB, 1 % NDB);
+      float mx0 = kNegInf, mx1 = kNegInf, m_new = 0.f, m_use = 0.f, alpha = 1.f, rs = 0.f;
 #pragma unroll
-      for (int i = 0; i < NDB * BC / 16; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS reads
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
+      for (int i = 0; i < NPV; ++i) {
+        const bf16x8 a = a0;
+        a0 = a1;
+        if (i + 2 < NPV) a1 = to.read_tr(sV[vb], (i + 2) / NDB, (i + 2) % NDB);
+        oacc[i % NDB] = mfma_bf16(a, pb[i / NDB], oacc[i % NDB]);
+        if (i == 0) {
+#pragma unroll
+          for (int e = 0; e < NE / 2; ++e) mx0 = fmaxf(mx0, sacc[e / 16][e % 16]);
+        } else if (i == 1) {
+#pragma unroll
+          for (int e = NE / 2; e < NE; ++e) mx1 = fmaxf(mx1, sacc[e / 16][e % 16]);
+        } else if (i == 2) {
+          const float mx = pair_max(fmaxf(mx0, mx1));
+          const float mxs = (mx == kNegInf) ? kNegInf : mx * p.c;
+          m_new = (mxs > m_run + kRescaleSlack) ? mxs : m_run;
+          m_use = (m_new == kNegInf) ? 0.f : m_new;
+          alpha = fast_exp2(m_run - m_use);
+        } else {
+          const int s0 = ((i - 3) * NE) / NEXP, s1 = ((i - 2) * NE) / NEXP;
+#pragma unroll
+          for (int e = s0; e < s1; ++e) {
+            const float pv = fast_exp2(fmaf(sacc[e / 16][e % 16], p.c, -m_use));
+            sacc[e / 16][e % 16] = pv;
+            rs += pv;
+            if ((e & 7) == 7) {  // a group of 8 probabilities is complete: pack it
+              const int kb = e / 16, s8 = (e % 16) / 8;
+              pbn[2 * kb + s8] = pack_bf16x8(sacc[kb][8 * s8 + 0], sacc[kb][8 * s8 + 1], sacc[kb][8 * s8 + 2],
+                                             sacc[kb][8 * s8 + 3], sacc[kb][8 * s8 + 4], sacc[kb][8 * s8 + 5],
+                                             sacc[kb][8 * s8 + 6], sacc[kb][8 * s8 + 7]);
+            }
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
+      // Consume the slice results here so that no later pass sinks them past the
+      // rescale branch, out of the slices they were placed in.
+#pragma unroll
+      for (int i = 0; i < 2 * NKB; ++i) asm volatile("" : "+v"(pbn[i]));
+      asm volatile("" : "+v"(rs), "+v"(alpha), "+v"(m_new));
+      const float m_prev = m_run;
+      m_run = m_new;
+      l_run = l_run * alpha + rs;
       // alpha == 1 exactly when no row of this wave moved its reference max.
       if (__builtin_amdgcn_ballot_w64(m_run != m_prev)) {
 #pragma unroll
