@@ -183,8 +183,10 @@ struct TileCopy {
     } else {
 #pragma unroll
       for (int i = 0; i < PER_WAVE; ++i) {
-        const int over = max(row0 + row[i] - (nvalid - 1), 0);  // rows to step back to row nvalid - 1
-        __builtin_amdgcn_global_load_lds((gptr)(gt + off[i] - (int64_t)over * ld),
+        // Step back over rows past nvalid - 1 (at most ROWS of them, so the
+        // offset stays within the 32-bit range of off[]).
+        const int over = max(row0 + row[i] - (nvalid - 1), 0);
+        __builtin_amdgcn_global_load_lds((gptr)(gt + (off[i] - over * (int32_t)ld)),
                                          (lptr)(lds_tile + 8 * 64 * (i * NWAVES + wave)), 16, 0, 0);
       }
     }

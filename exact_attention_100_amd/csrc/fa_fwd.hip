@@ -147,9 +147,15 @@ void fwd_bf16_kernel(FwdKParams p) {
   constexpr int TILE = BC * D;
 
   // K and V tiles, double-buffered, row-major in the swizzled layout (16-byte
-  // row reads for the K operand, transposing reads for the V^T operand).
-  __shared__ __attribute__((aligned(16))) bf16 sK[2][TILE];
-  __shared__ __attribute__((aligned(16))) bf16 sV[2][TILE];
+  // row reads for the K operand, transposing reads for the V^T operand). The
+  // four buffers are separate arrays and every access names one of them
+  // statically (the key loop is unrolled by two): the compiler can then tell
+  // that a read of one buffer does not depend on the direct global -> LDS
+  // copies still in flight into another, and does not wait for them.
+  __shared__ __attribute__((aligned(16))) bf16 sK0[TILE];
+  __shared__ __attribute__((aligned(16))) bf16 sK1[TILE];
+  __shared__ __attribute__((aligned(16))) bf16 sV0[TILE];
+  __shared__ __attribute__((aligned(16))) bf16 sV1[TILE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5;
@@ -197,7 +203,8 @@ void fwd_bf16_kernel(FwdKParams p) {
   const int nt = rg.n_tiles;
   auto kv0_of = [&](int t) { return fwd_tile_kv0<BC, SPARSE>(p, rg, min(t, nt - 1)); };
 
-  auto s_mfma = [&](int buf, f32x16 (&sacc)[NKB]) {  // S^T (keys x queries) = K_tile Q^T
+  auto s_mfma = [&](const bf16* sk, f32x16 (&sacc)[NKB]) __attribute__((always_inline)) {
+    // S^T (keys x queries) = K_tile Q^T
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -205,15 +212,15 @@ void fwd_bf16_kernel(FwdKParams p) {
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) sacc[kb] = mfma_bf16(to.read_row(sK[buf], kb, kk), qf[kk], sacc[kb]);
+      for (int kb = 0; kb < NKB; ++kb) sacc[kb] = mfma_bf16(to.read_row(sk, kb, kk), qf[kk], sacc[kb]);
   };
   // O^T (dims x queries) += V^T P^T; A = V^T through the transposing LDS read,
   // whose key slots are the same as those of pb.
-  auto pv_mfma = [&](int buf, const bf16x8 (&pb)[2 * NKB]) {
+  auto pv_mfma = [&](const bf16* sv, const bf16x8 (&pb)[2 * NKB]) __attribute__((always_inline)) {
 #pragma unroll
     for (int ks = 0; ks < BC / 16; ++ks)
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) oacc[db] = mfma_bf16(to.read_tr(sV[buf], ks, db), pb[ks], oacc[db]);
+      for (int db = 0; db < NDB; ++db) oacc[db] = mfma_bf16(to.read_tr(sv, ks, db), pb[ks], oacc[db]);
   };
   // Online softmax of one tile, then P^T packed as B operands: k-step ks = 2 kb + s
   // covers keys 32 kb + 16 s + {4g..4g+3, 8+4g..8+4g+3}, registers 8 s .. 8 s + 7 of block kb.
@@ -234,26 +241,27 @@ void fwd_bf16_kernel(FwdKParams p) {
 
   if (nt > 0) {
     bf16x8 pb[2 * NKB];
-    cp.issue(sK[0], Kh, p.sn, kv0_of(0), N);
+    cp.issue(sK0, Kh, p.sn, kv0_of(0), N);
     wait_vmem();
     __syncthreads();
-    cp.issue(sK[1], Kh, p.sn, kv0_of(1), N);
-    cp.issue(sV[0], Vh, p.sn, kv0_of(0), N);
+    cp.issue(sK1, Kh, p.sn, kv0_of(1), N);
+    cp.issue(sV0, Vh, p.sn, kv0_of(0), N);
     {
       f32x16 sacc[NKB];
-      s_mfma(0, sacc);
+      s_mfma(sK0, sacc);
       if (needs_mask(kv0_of(0))) mask_tile<NKB>(sacc, kv0_of(0), rg.kv_len, p.causal, qrow, g);
       softmax_pack(sacc, pb);  // (alpha is irrelevant: nothing has been accumulated yet)
     }
     wait_vmem();
     __syncthreads();
 
-    for (int t = 1; t < nt; ++t) {
+    // Iteration t: K_{t+1} -> kw, V_t -> vw, S(t) from kr, P V of tile t - 1 from vr.
+    auto iteration = [&](int t, bf16* kw, const bf16* kr, bf16* vw, const bf16* vr) __attribute__((always_inline)) {
       const int kv0 = kv0_of(t);
-      cp.issue(sK[(t + 1) & 1], Kh, p.sn, kv0_of(t + 1), N);
-      cp.issue(sV[t & 1], Vh, p.sn, kv0, N);
+      cp.issue(kw, Kh, p.sn, kv0_of(t + 1), N);
+      cp.issue(vw, Vh, p.sn, kv0, N);
       f32x16 sacc[NKB];
-      s_mfma(t & 1, sacc);
+      s_mfma(kr, sacc);
       if (needs_mask(kv0)) mask_tile<NKB>(sacc, kv0, rg.kv_len, p.causal, qrow, g);
 
       // The P V of tile t - 1 and the softmax of tile t are independent. They are
@@ -265,16 +273,15 @@ void fwd_bf16_kernel(FwdKParams p) {
       constexpr int NE = NKB * 16;  // scores per lane
       constexpr int NEXP = NPV - 3; // slices doing exponentials
       static_assert(NPV >= 4, "too few MFMAs to interleave");
-      const int vb = (t - 1) & 1;
       bf16x8 pbn[2 * NKB];
-      bf16x8 a0 = to.read_tr(sV[vb], 0, 0);
-      bf16x8 a1 = to.read_tr(sV[vb], 1 / NDB, 1 % NDB);
+      bf16x8 a0 = to.read_tr(vr, 0, 0);
+      bf16x8 a1 = to.read_tr(vr, 1 / NDB, 1 % NDB);
       float mx0 = kNegInf, mx1 = kNegInf, m_new = 0.f, m_use = 0.f, alpha = 1.f, rs = 0.f;
 #pragma unroll
       for (int i = 0; i < NPV; ++i) {
         const bf16x8 a = a0;
         a0 = a1;
-        if (i + 2 < NPV) a1 = to.read_tr(sV[vb], (i + 2) / NDB, (i + 2) % NDB);
+        if (i + 2 < NPV) a1 = to.read_tr(vr, (i + 2) / NDB, (i + 2) % NDB);
         oacc[i % NDB] = mfma_bf16(a, pb[i / NDB], oacc[i % NDB]);
         if (i == 0) {
 #pragma unroll
@@ -322,8 +329,14 @@ void fwd_bf16_kernel(FwdKParams p) {
       for (int i = 0; i < 2 * NKB; ++i) pb[i] = pbn[i];
       wait_vmem();
       __syncthreads();
+    };
+    for (int t = 1; t < nt; t += 2) {
+      iteration(t, sK0, sK1, sV1, sV0);
+      if (t + 1 < nt) iteration(t + 1, sK1, sK0, sV0, sV1);
     }
-    pv_mfma((nt - 1) & 1, pb);
+    // The last tile's V is in sV1 when nt is even, in sV0 when nt is odd.
+    if (nt & 1) pv_mfma(sV0, pb);
+    else pv_mfma(sV1, pb);
   }
 
   // Epilogue: O = O_acc / l, LSE = (m + log2 l) ln 2. Rows with no key: O = 0, LSE = -inf.
