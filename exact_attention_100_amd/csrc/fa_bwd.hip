@@ -115,10 +115,17 @@ void bwd_dkdv_kernel(BwdKParams p) {
   constexpr int TILE = BRQ * D;
   static_assert(BRQ <= 64, "row statistics use one 64-lane copy");
 
-  __shared__ __attribute__((aligned(16))) bf16 sQ[2][TILE];
-  __shared__ __attribute__((aligned(16))) bf16 sdO[2][TILE];
-  __shared__ __attribute__((aligned(16))) float sL[2][64];
-  __shared__ __attribute__((aligned(16))) float sDl[2][64];
+  // Double buffers as separate arrays, each access naming one statically (the
+  // query-tile loop is unrolled by two), so that LDS reads of the current tile
+  // do not wait for the copies of the next tile still in flight.
+  __shared__ __attribute__((aligned(16))) bf16 sQ0[TILE];
+  __shared__ __attribute__((aligned(16))) bf16 sQ1[TILE];
+  __shared__ __attribute__((aligned(16))) bf16 sdO0[TILE];
+  __shared__ __attribute__((aligned(16))) bf16 sdO1[TILE];
+  __shared__ __attribute__((aligned(16))) float sL0[64];
+  __shared__ __attribute__((aligned(16))) float sL1[64];
+  __shared__ __attribute__((aligned(16))) float sDl0[64];
+  __shared__ __attribute__((aligned(16))) float sDl1[64];
   __shared__ __attribute__((aligned(16))) bf16 sV[VLDS ? kBwdBlock * D : 8];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -192,24 +199,26 @@ void bwd_dkdv_kernel(BwdKParams p) {
     cp.init(wu, lane, p.sn);
     TileOffsets<D> to;
     to.init(lane);
-    auto issue_tile = [&](int q0, int buf) {
-      cp.issue(sQ[buf], Qh, p.sn, q0, N);
-      cp.issue(sdO[buf], dOh, p.sn, q0, N);
-      if (wave == 0) vec_dma64(sL[buf], p.lse2 + rowbase, q0, N, lane);
-      if (wave == 1) vec_dma64(sDl[buf], p.delta + rowbase, q0, N, lane);
+    auto issue_tile = [&](int q0, bf16* qw, bf16* dow, float* lw, float* dlw) __attribute__((always_inline)) {
+      cp.issue(qw, Qh, p.sn, q0, N);
+      cp.issue(dow, dOh, p.sn, q0, N);
+      if (wave == 0) vec_dma64(lw, p.lse2 + rowbase, q0, N, lane);
+      if (wave == 1) vec_dma64(dlw, p.delta + rowbase, q0, N, lane);
     };
 
-    issue_tile(tile_q0(0), 0);
+    issue_tile(tile_q0(0), sQ0, sdO0, sL0, sDl0);
     wait_vmem();
     __syncthreads();
 
-    for (int t = 0; t < n_qt; ++t) {
-      const int cur = t & 1;
+    // Iteration t reads tile t from (qr, dor, lr, dlr) and copies tile t + 1
+    // into (qw, dow, lw, dlw).
+    auto iteration = [&](int t, const bf16* qr, const bf16* dor, const float* lr, const float* dlr, bf16* qw,
+                         bf16* dow, float* lw, float* dlw) __attribute__((always_inline)) {
       const int q0 = tile_q0(t);
-      // Prefetch the next tile into the idle buffer (the last iteration re-reads
-      // its own tile); every wave finished reading that buffer before the
-      // previous barrier.
-      issue_tile(tile_q0(min(t + 1, n_qt - 1)), cur ^ 1);
+      to.refresh();
+      // Prefetch the next tile into the idle buffers (the last iteration re-reads
+      // its own tile); every wave finished reading them before the previous barrier.
+      issue_tile(tile_q0(min(t + 1, n_qt - 1)), qw, dow, lw, dlw);
 
       // S = Q_i K_w^T and dP = dO_i V_w^T (rows = queries, columns = this wave's keys).
       f32x16 sacc[NQB], dpacc[NQB];
@@ -229,8 +238,8 @@ void bwd_dkdv_kernel(BwdKParams p) {
             vb = to.read_row(sV, wu, kk);
           else
             vb = vf[kk];
-          sacc[sb] = mfma_bf16(to.read_row(sQ[cur], sb, kk), kf[kk], sacc[sb]);
-          dpacc[sb] = mfma_bf16(to.read_row(sdO[cur], sb, kk), vb, dpacc[sb]);
+          sacc[sb] = mfma_bf16(to.read_row(qr, sb, kk), kf[kk], sacc[sb]);
+          dpacc[sb] = mfma_bf16(to.read_row(dor, sb, kk), vb, dpacc[sb]);
         }
 
       // P = 2^(c S - lse2), dS = P (dP - D). Register r of sub-block sb is query
@@ -253,8 +262,8 @@ void bwd_dkdv_kernel(BwdKParams p) {
       for (int sb = 0; sb < NQB; ++sb)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const f32x4 lv = *reinterpret_cast<const f32x4*>(&sL[cur][32 * sb + 8 * j + 4 * g]);
-          const f32x4 dv = *reinterpret_cast<const f32x4*>(&sDl[cur][32 * sb + 8 * j + 4 * g]);
+          const f32x4 lv = *reinterpret_cast<const f32x4*>(&lr[32 * sb + 8 * j + 4 * g]);
+          const f32x4 dv = *reinterpret_cast<const f32x4*>(&dlr[32 * sb + 8 * j + 4 * g]);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int r = 4 * j + i;
@@ -285,12 +294,16 @@ void bwd_dkdv_kernel(BwdKParams p) {
       for (int qs = 0; qs < 2 * NQB; ++qs)
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          dvacc[db] = mfma_bf16(to.read_tr(sdO[cur], qs, db), pb[qs], dvacc[db]);
-          dkacc[db] = mfma_bf16(to.read_tr(sQ[cur], qs, db), dsb[qs], dkacc[db]);
+          dvacc[db] = mfma_bf16(to.read_tr(dor, qs, db), pb[qs], dvacc[db]);
+          dkacc[db] = mfma_bf16(to.read_tr(qr, qs, db), dsb[qs], dkacc[db]);
         }
 
       wait_vmem();
       __syncthreads();
+    };
+    for (int t = 0; t < n_qt; t += 2) {
+      iteration(t, sQ0, sdO0, sL0, sDl0, sQ1, sdO1, sL1, sDl1);
+      if (t + 1 < n_qt) iteration(t + 1, sQ1, sdO1, sL1, sDl1, sQ0, sdO0, sL0, sDl0);
     }
   }
 
@@ -339,8 +352,13 @@ void bwd_dq_kernel(BwdKParams p) {
   constexpr int NKK = D / 16;
   constexpr int TILE = BC * D;
 
-  __shared__ __attribute__((aligned(16))) bf16 sK[2][TILE];
-  __shared__ __attribute__((aligned(16))) bf16 sV[2][TILE];
+  // Double buffers as separate arrays, named statically (the key-tile loop is
+  // unrolled by two) so that reads of the current tile do not wait for the
+  // copies of the next.
+  __shared__ __attribute__((aligned(16))) bf16 sK0[TILE];
+  __shared__ __attribute__((aligned(16))) bf16 sK1[TILE];
+  __shared__ __attribute__((aligned(16))) bf16 sV0[TILE];
+  __shared__ __attribute__((aligned(16))) bf16 sV1[TILE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5;
@@ -402,18 +420,19 @@ void bwd_dq_kernel(BwdKParams p) {
   cp.init(uniform_wave_id(), lane, p.sn);
   TileOffsets<D> to;
   to.init(lane);
-  auto issue_tile = [&](int kv0, int buf) {
-    cp.issue(sK[buf], Kh, p.sn, kv0, N);
-    cp.issue(sV[buf], Vh, p.sn, kv0, N);
+  auto issue_tile = [&](int kv0, bf16* kw, bf16* vw) __attribute__((always_inline)) {
+    cp.issue(kw, Kh, p.sn, kv0, N);
+    cp.issue(vw, Vh, p.sn, kv0, N);
   };
-  issue_tile(tile_kv0(0), 0);
+  issue_tile(tile_kv0(0), sK0, sV0);
   wait_vmem();
   __syncthreads();
 
-  for (int t = 0; t < n_tiles; ++t) {
-    const int buf = t & 1;
+  // Iteration t reads tile t from (kr, vr) and copies tile t + 1 into (kw, vw).
+  auto iteration = [&](int t, const bf16* kr, const bf16* vr, bf16* kw, bf16* vw) __attribute__((always_inline)) {
     const int kv0 = tile_kv0(t);
-    issue_tile(tile_kv0(min(t + 1, n_tiles - 1)), buf ^ 1);
+    to.refresh();
+    issue_tile(tile_kv0(min(t + 1, n_tiles - 1)), kw, vw);
 
     // S^T and dP^T (keys x queries).
     f32x16 sacc[NKB], dpacc[NKB];
@@ -428,8 +447,8 @@ void bwd_dq_kernel(BwdKParams p) {
     for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        sacc[kb] = mfma_bf16(to.read_row(sK[buf], kb, kk), qf[kk], sacc[kb]);
-        dpacc[kb] = mfma_bf16(to.read_row(sV[buf], kb, kk), df[kk], dpacc[kb]);
+        sacc[kb] = mfma_bf16(to.read_row(kr, kb, kk), qf[kk], sacc[kb]);
+        dpacc[kb] = mfma_bf16(to.read_row(vr, kb, kk), df[kk], dpacc[kb]);
       }
 
     // dS^T = P^T (dP^T - D); register r of block kb is key kv0 + 32 kb + 8 (r/4) + 4 g + r%4.
@@ -469,10 +488,14 @@ void bwd_dq_kernel(BwdKParams p) {
     for (int ks = 0; ks < BC / 16; ++ks)
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
-        dqacc[db] = mfma_bf16(to.read_tr(sK[buf], ks, db), dsb[ks], dqacc[db]);
+        dqacc[db] = mfma_bf16(to.read_tr(kr, ks, db), dsb[ks], dqacc[db]);
 
     wait_vmem();
     __syncthreads();
+  };
+  for (int t = 0; t < n_tiles; t += 2) {
+    iteration(t, sK0, sV0, sK1, sV1);
+    if (t + 1 < n_tiles) iteration(t + 1, sK1, sV1, sK0, sV0);
   }
 
   // dQ = scale dQ^T^T: lane = query, register r = dim 32 db + 8 (r/4) + 4 g + r%4.

@@ -215,6 +215,16 @@ struct TileOffsets {
       tr_hi[mb] = tile_off<COLS>(r + 8, c);
     }
   }
+  // Makes the offsets opaque to the optimiser at this point. Called once per
+  // loop iteration, it keeps buffer + offset sums from being hoisted out of the
+  // loop as separate registers per buffer: each read then adds the buffer's
+  // static base as the LDS instruction's immediate offset instead.
+  __device__ __forceinline__ void refresh() {
+#pragma unroll
+    for (int i = 0; i < COLS / 16; ++i) asm volatile("" : "+v"(row[i]));
+#pragma unroll
+    for (int i = 0; i < COLS / 32; ++i) asm volatile("" : "+v"(tr_lo[i]), "+v"(tr_hi[i]));
+  }
   __device__ __forceinline__ bf16x8 read_row(const bf16* X, int b, int kk) const {
     return *reinterpret_cast<const bf16x8*>(X + b * 32 * COLS + row[kk]);
   }

@@ -258,6 +258,7 @@ void fwd_bf16_kernel(FwdKParams p) {
     // Iteration t: K_{t+1} -> kw, V_t -> vw, S(t) from kr, P V of tile t - 1 from vr.
     auto iteration = [&](int t, bf16* kw, const bf16* kr, bf16* vw, const bf16* vr) __attribute__((always_inline)) {
       const int kv0 = kv0_of(t);
+      to.refresh();
       cp.issue(kw, Kh, p.sn, kv0_of(t + 1), N);
       cp.issue(vw, Vh, p.sn, kv0, N);
       f32x16 sacc[NKB];
