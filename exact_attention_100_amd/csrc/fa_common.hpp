@@ -193,12 +193,67 @@ struct TileCopy {
   }
 };
 
-// Loop-invariant per-lane element offsets into swizzled [rows x COLS] tiles.
+// LDS reads issued as inline assembly, for loops that manage their own waits.
+// While a direct global -> LDS copy is in flight the compiler only ever waits
+// for all LDS reads at once (lgkmcnt(0)); LDS reads return in order and those
+// copies are counted by vmcnt alone, so a loop that knows how many reads it
+// issued after the one it needs can wait for exactly that one (lds_wait). The
+// byte offset `off` must fold to a constant; the common tile offsets become the
+// instruction's immediate. The caller makes sure (barriers) the data is there.
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+#define FA_DS_OFFSETS(X) X(0) X(1024) X(2048) X(3072) X(4096) X(6144) X(8192) X(12288) X(16384) X(24576)
+__device__ __forceinline__ bf16x8 lds_read_b128_asm(uint32_t addr, int off) {
+  u32x4 v;
+  switch (off) {
+#define FA_CASE(O) \
+  case O:          \
+    asm volatile("ds_read_b128 %0, %1 offset:" #O : "=v"(v) : "v"(addr)); \
+    break;
+    FA_DS_OFFSETS(FA_CASE)
+#undef FA_CASE
+    default:
+      asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr + off));
+  }
+  return __builtin_bit_cast(bf16x8, v);
+}
+__device__ __forceinline__ bf16x4 lds_read_tr_asm(uint32_t addr, int off) {
+  u32x2 v;
+  switch (off) {
+#define FA_CASE(O) \
+  case O:          \
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:" #O : "=v"(v) : "v"(addr)); \
+    break;
+    FA_DS_OFFSETS(FA_CASE)
+#undef FA_CASE
+    default:
+      asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(addr + off));
+  }
+  return __builtin_bit_cast(bf16x4, v);
+}
+// s_waitcnt lgkmcnt(n) (vmcnt and expcnt left alone); n must fold to a constant.
+__device__ __forceinline__ void lds_wait(int n) {
+  switch (n) {
+#define FA_W(N) \
+  case N:       \
+    __builtin_amdgcn_s_waitcnt(0xC07F | ((N) << 8)); \
+    break;
+    FA_W(0) FA_W(1) FA_W(2) FA_W(3) FA_W(4) FA_W(5) FA_W(6) FA_W(7)
+    FA_W(8) FA_W(9) FA_W(10) FA_W(11) FA_W(12) FA_W(13) FA_W(14)
+#undef FA_W
+    default:
+      __builtin_amdgcn_s_waitcnt(0xC07F | (15 << 8));
+  }
+}
+
+// Loop-invariant per-lane byte offsets into swizzled [rows x COLS] bf16 tiles
+// (bytes, so that an LDS address is the offset plus an immediate).
 // Row reads: the MFMA A operand of rows 32 b + l32 at k-step kk (16 columns,
-// lane group g taking columns 8 g .. 8 g + 7) lives at b * 32 * COLS + row[kk]
-// (the swizzle depends only on the row's low four bits).
+// lane group g taking columns 8 g .. 8 g + 7) lives at element
+// b * 32 * COLS + row[kk] / 2 (the swizzle depends only on the row's low four bits).
 // Transposing reads (lds_read_tr_k16_swz) at k0 = 16 ks, m0 = 32 mb read
-// 16 ks * COLS + tr_lo[mb] and 16 ks * COLS + tr_hi[mb].
+// elements 16 ks * COLS + tr_lo[mb] / 2 and 16 ks * COLS + tr_hi[mb] / 2.
 template <int COLS>
 struct TileOffsets {
   int32_t row[COLS / 16];
@@ -206,13 +261,13 @@ struct TileOffsets {
   __device__ __forceinline__ void init(int lane) {
     const int l32 = lane & 31, g = lane >> 5, h = (lane >> 4) & 1, j = lane & 15;
 #pragma unroll
-    for (int kk = 0; kk < COLS / 16; ++kk) row[kk] = tile_off<COLS>(l32, 16 * kk + 8 * g);
+    for (int kk = 0; kk < COLS / 16; ++kk) row[kk] = 2 * tile_off<COLS>(l32, 16 * kk + 8 * g);
     const int r = 4 * g + (j >> 2);
 #pragma unroll
     for (int mb = 0; mb < COLS / 32; ++mb) {
       const int c = 32 * mb + 16 * h + 4 * (j & 3);
-      tr_lo[mb] = tile_off<COLS>(r, c);
-      tr_hi[mb] = tile_off<COLS>(r + 8, c);
+      tr_lo[mb] = 2 * tile_off<COLS>(r, c);
+      tr_hi[mb] = 2 * tile_off<COLS>(r + 8, c);
     }
   }
   // Makes the offsets opaque to the optimiser at this point. Called once per
@@ -226,11 +281,21 @@ struct TileOffsets {
     for (int i = 0; i < COLS / 32; ++i) asm volatile("" : "+v"(tr_lo[i]), "+v"(tr_hi[i]));
   }
   __device__ __forceinline__ bf16x8 read_row(const bf16* X, int b, int kk) const {
-    return *reinterpret_cast<const bf16x8*>(X + b * 32 * COLS + row[kk]);
+    const char* p = reinterpret_cast<const char*>(X + b * 32 * COLS) + row[kk];
+    return *reinterpret_cast<const bf16x8*>(p);
+  }
+  // The same reads as inline assembly (lds_read_*_asm; base = lds_address of X):
+  // the caller waits for them itself (lds_wait).
+  __device__ __forceinline__ bf16x8 read_row_asm(uint32_t base, int b, int kk) const {
+    return lds_read_b128_asm(base + row[kk], b * 64 * COLS);
+  }
+  __device__ __forceinline__ bf16x8 read_tr_asm(uint32_t base, int ks, int mb) const {
+    return concat_bf16x4(lds_read_tr_asm(base + tr_lo[mb], 32 * ks * COLS),
+                         lds_read_tr_asm(base + tr_hi[mb], 32 * ks * COLS));
   }
   __device__ __forceinline__ bf16x8 read_tr(const bf16* X, int ks, int mb) const {
     typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-    const bf16* p = X + 16 * ks * COLS;
+    const char* p = reinterpret_cast<const char*>(X + 16 * ks * COLS);
     const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + tr_lo[mb]));
     const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + tr_hi[mb]));
     return concat_bf16x4(lo, hi);

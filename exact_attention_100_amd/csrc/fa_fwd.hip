@@ -132,6 +132,56 @@ __device__ __forceinline__ float online_softmax_step(f32x16 (&s)[NKB], float c, 
 
 // ----------------------------------------------------------------------------------- bf16
 
+// acc + the sum of the 8 bf16 values of one packed operand (v_dot2 against ones).
+__device__ __forceinline__ float sum_bf16x8(bf16x8 v, float acc) {
+  const u32x4 u = __builtin_bit_cast(u32x4, v);
+  const bf16x2 one = {(bf16)1.f, (bf16)1.f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    // (Through a scalar copy: this compiler's __builtin_bit_cast of a vector
+    // element expression reads element 0 whatever the index.)
+    const uint32_t w = u[i];
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), one, acc, false);
+  }
+  return acc;
+}
+
+// The bf16 kernels' softmax step: as online_softmax_step, but the probabilities
+// are packed to bf16 (pb, the B operands of the P V product; k-step ks = 2 kb + s
+// holds registers 8 s .. 8 s + 7 of block kb) and the row sum adds up those
+// rounded values. The normaliser is then the sum of exactly the weights the
+// product applies, so O is a convex combination of V rows: a bf16 rounding of a
+// dominant probability cancels instead of scaling O. (LSE then carries that
+// rounding, at most ln(1 + 2^-8) in a row with a single dominant key.)
+template <int NKB>
+__device__ __forceinline__ float softmax_tile_bf16(f32x16 (&s)[NKB], float c, float& m_run, float& l_run,
+                                                   bf16x8 (&pb)[2 * NKB]) {
+  float mx = kNegInf;
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+  mx = pair_max(mx);
+  const float mxs = (mx == kNegInf) ? kNegInf : mx * c;
+  const float m_new = (mxs > m_run + kRescaleSlack) ? mxs : m_run;
+  const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+  const float alpha = fast_exp2(m_run - m_use);
+  m_run = m_new;
+  float rs = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+    for (int sh = 0; sh < 2; ++sh) {
+#pragma unroll
+      for (int i = 8 * sh; i < 8 * sh + 8; ++i) s[kb][i] = fast_exp2(fmaf(s[kb][i], c, -m_use));
+      pb[2 * kb + sh] = pack_bf16x8(s[kb][8 * sh + 0], s[kb][8 * sh + 1], s[kb][8 * sh + 2], s[kb][8 * sh + 3],
+                                    s[kb][8 * sh + 4], s[kb][8 * sh + 5], s[kb][8 * sh + 6], s[kb][8 * sh + 7]);
+      rs = sum_bf16x8(pb[2 * kb + sh], rs);
+    }
+  l_run = l_run * alpha + rs;
+  return alpha;
+}
+
 // Waves per SIMD the bf16 forward is compiled for: two, so that one wave's
 // softmax (VALU, transcendental) overlaps the other wave's MFMA work.
 #ifndef FA_FWD_WAVES_PER_EU
@@ -203,16 +253,29 @@ void fwd_bf16_kernel(FwdKParams p) {
   const int nt = rg.n_tiles;
   auto kv0_of = [&](int t) { return fwd_tile_kv0<BC, SPARSE>(p, rg, min(t, nt - 1)); };
 
+  // S^T (keys x queries) = K_tile Q^T. MFMA j is k-step j / NKB of key block j % NKB.
+  // The K operands are inline-assembly LDS reads kAhead MFMAs ahead of their
+  // use, each waited for exactly (lds_wait): with copies in flight the compiler
+  // would drain every LDS read before each product.
   auto s_mfma = [&](const bf16* sk, f32x16 (&sacc)[NKB]) __attribute__((always_inline)) {
-    // S^T (keys x queries) = K_tile Q^T
+    constexpr int NS = NKK * NKB, kAhead = 4;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+    const uint32_t base = lds_address(sk);
+    bf16x8 ring[kAhead];
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk)
+    for (int j = 0; j < kAhead; ++j) ring[j] = to.read_row_asm(base, j % NKB, j / NKB);
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) sacc[kb] = mfma_bf16(to.read_row(sk, kb, kk), qf[kk], sacc[kb]);
+    for (int j = 0; j < NS; ++j) {
+      const bf16x8 a = ring[j % kAhead];
+      if (j + kAhead < NS) ring[j % kAhead] = to.read_row_asm(base, (j + kAhead) % NKB, (j + kAhead) / NKB);
+      lds_wait(NS - 1 - j < kAhead ? NS - 1 - j : kAhead);  // the reads issued after operand j
+      __builtin_amdgcn_sched_barrier(0);
+      sacc[j % NKB] = mfma_bf16(a, qf[j / NKB], sacc[j % NKB]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
   // O^T (dims x queries) += V^T P^T; A = V^T through the transposing LDS read,
   // whose key slots are the same as those of pb.
@@ -221,19 +284,6 @@ void fwd_bf16_kernel(FwdKParams p) {
     for (int ks = 0; ks < BC / 16; ++ks)
 #pragma unroll
       for (int db = 0; db < NDB; ++db) oacc[db] = mfma_bf16(to.read_tr(sv, ks, db), pb[ks], oacc[db]);
-  };
-  // Online softmax of one tile, then P^T packed as B operands: k-step ks = 2 kb + s
-  // covers keys 32 kb + 16 s + {4g..4g+3, 8+4g..8+4g+3}, registers 8 s .. 8 s + 7 of block kb.
-  auto softmax_pack = [&](f32x16 (&sacc)[NKB], bf16x8 (&pb)[2 * NKB]) -> float {
-    const float alpha = online_softmax_step<NKB>(sacc, p.c, m_run, l_run);
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int s = 0; s < 2; ++s)
-        pb[2 * kb + s] = pack_bf16x8(sacc[kb][8 * s + 0], sacc[kb][8 * s + 1], sacc[kb][8 * s + 2],
-                                     sacc[kb][8 * s + 3], sacc[kb][8 * s + 4], sacc[kb][8 * s + 5],
-                                     sacc[kb][8 * s + 6], sacc[kb][8 * s + 7]);
-    return alpha;
   };
   auto needs_mask = [&](int kv0) {
     return !SPARSE && ((kv0 + BC > rg.kv_len) || (p.causal && kv0 + BC - 1 > q0 + wave * 32));
@@ -250,7 +300,9 @@ void fwd_bf16_kernel(FwdKParams p) {
       f32x16 sacc[NKB];
       s_mfma(sK0, sacc);
       if (needs_mask(kv0_of(0))) mask_tile<NKB>(sacc, kv0_of(0), rg.kv_len, p.causal, qrow, g);
-      softmax_pack(sacc, pb);  // (alpha is irrelevant: nothing has been accumulated yet)
+      // P^T as B operands: k-step ks = 2 kb + s covers keys 32 kb + 16 s +
+      // {4g..4g+3, 8+4g..8+4g+3}. (alpha is irrelevant: nothing accumulated yet.)
+      softmax_tile_bf16<NKB>(sacc, p.c, m_run, l_run, pb);
     }
     wait_vmem();
     __syncthreads();
@@ -275,14 +327,17 @@ void fwd_bf16_kernel(FwdKParams p) {
       constexpr int NEXP = NPV - 3; // slices doing exponentials
       static_assert(NPV >= 4, "too few MFMAs to interleave");
       bf16x8 pbn[2 * NKB];
-      bf16x8 a0 = to.read_tr(vr, 0, 0);
-      bf16x8 a1 = to.read_tr(vr, 1 / NDB, 1 % NDB);
+      const uint32_t vbase = lds_address(vr);
+      bf16x8 a0 = to.read_tr_asm(vbase, 0, 0);
+      bf16x8 a1 = to.read_tr_asm(vbase, 1 / NDB, 1 % NDB);
       float mx0 = kNegInf, mx1 = kNegInf, m_new = 0.f, m_use = 0.f, alpha = 1.f, rs = 0.f;
 #pragma unroll
       for (int i = 0; i < NPV; ++i) {
         const bf16x8 a = a0;
         a0 = a1;
-        if (i + 2 < NPV) a1 = to.read_tr(vr, (i + 2) / NDB, (i + 2) % NDB);
+        if (i + 2 < NPV) a1 = to.read_tr_asm(vbase, (i + 2) / NDB, (i + 2) % NDB);
+        lds_wait(2 * ((i + 2 < NPV ? i + 2 : NPV - 1) - i));  // two reads per later operand
+        __builtin_amdgcn_sched_barrier(0);
         oacc[i % NDB] = mfma_bf16(a, pb[i / NDB], oacc[i % NDB]);
         if (i == 0) {
 #pragma unroll
@@ -300,14 +355,13 @@ void fwd_bf16_kernel(FwdKParams p) {
           const int s0 = ((i - 3) * NE) / NEXP, s1 = ((i - 2) * NE) / NEXP;
 #pragma unroll
           for (int e = s0; e < s1; ++e) {
-            const float pv = fast_exp2(fmaf(sacc[e / 16][e % 16], p.c, -m_use));
-            sacc[e / 16][e % 16] = pv;
-            rs += pv;
-            if ((e & 7) == 7) {  // a group of 8 probabilities is complete: pack it
+            sacc[e / 16][e % 16] = fast_exp2(fmaf(sacc[e / 16][e % 16], p.c, -m_use));
+            if ((e & 7) == 7) {  // a group of 8 probabilities is complete: pack and sum it
               const int kb = e / 16, s8 = (e % 16) / 8;
               pbn[2 * kb + s8] = pack_bf16x8(sacc[kb][8 * s8 + 0], sacc[kb][8 * s8 + 1], sacc[kb][8 * s8 + 2],
                                              sacc[kb][8 * s8 + 3], sacc[kb][8 * s8 + 4], sacc[kb][8 * s8 + 5],
                                              sacc[kb][8 * s8 + 6], sacc[kb][8 * s8 + 7]);
+              rs = sum_bf16x8(pbn[2 * kb + s8], rs);
             }
           }
         }

