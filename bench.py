@@ -219,10 +219,10 @@ def main():
             fa.bwd(t["q"], t["k"], t["v"], o, t["do"], lse, scale=sc, causal=case.causal, key_len=key_len,
                    dq=dq, dk=dk, dv=dv, workspace=ws)
         else:
-            fa.blocksparse_fwd(t["q"], t["k"], t["v"], bmask, case.block_size, scale=sc, out=o, lse=lse,
-                               workspace=ws)
+            fa.blocksparse_fwd(t["q"], t["k"], t["v"], bmask, case.block_size, scale=sc, causal=case.causal,
+                               key_len=key_len, out=o, lse=lse, workspace=ws)
             fa.blocksparse_bwd(t["q"], t["k"], t["v"], o, t["do"], lse, bmask, case.block_size, scale=sc,
-                               dq=dq, dk=dk, dv=dv, workspace=ws)
+                               causal=case.causal, key_len=key_len, dq=dq, dk=dk, dv=dv, workspace=ws)
 
     for _ in range(args.warmup):
         step()

@@ -154,12 +154,15 @@ def _mask_check(block_mask, q, block_size):
         raise ValueError("block_mask must be a contiguous uint8 [N/bs, N/bs] tensor on the same device")
 
 
-def blocksparse_fwd(q, k, v, block_mask, block_size, scale=None, out=None, lse=None, workspace=None):
-    """Block-sparse forward (zero blocks of block_mask skipped); returns (O, LSE)."""
+def blocksparse_fwd(q, k, v, block_mask, block_size, scale=None, causal=False, key_len=None, out=None,
+                    lse=None, workspace=None):
+    """Block-sparse forward (zero blocks of block_mask skipped, combined by AND with the causal
+    and key-length masks); returns (O, LSE)."""
     torch = _torch()
     d = _desc(q)
     _same_layout(q, k, v)
     _mask_check(block_mask, q, block_size)
+    kl = _key_len(key_len, q)
     o = _empty_like(q) if out is None else out
     B, H, N, _ = q.shape
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
@@ -167,20 +170,21 @@ def blocksparse_fwd(q, k, v, block_mask, block_size, scale=None, out=None, lse=N
     need = int(lib().fa_blocksparse_workspace_bytes(ctypes.byref(d), int(block_size), 0))
     ws = _workspace(need, q, workspace)
     st = lib().fa_blocksparse_fwd(ctypes.byref(d), q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                                  _scale(scale, q.shape[-1]), block_mask.data_ptr(), int(block_size),
-                                  o.data_ptr(), lse.data_ptr(), ws.data_ptr(), ws.numel() * ws.element_size(),
-                                  _stream(q))
+                                  _scale(scale, q.shape[-1]), int(bool(causal)), _ptr(kl),
+                                  block_mask.data_ptr(), int(block_size), o.data_ptr(), lse.data_ptr(),
+                                  ws.data_ptr(), ws.numel() * ws.element_size(), _stream(q))
     _check(st, "fa_blocksparse_fwd")
     return o, lse
 
 
-def blocksparse_bwd(q, k, v, o, do, lse, block_mask, block_size, scale=None, dq=None, dk=None, dv=None,
-                    workspace=None):
-    """Block-sparse backward; returns (dQ, dK, dV)."""
+def blocksparse_bwd(q, k, v, o, do, lse, block_mask, block_size, scale=None, causal=False, key_len=None,
+                    dq=None, dk=None, dv=None, workspace=None):
+    """Block-sparse backward; returns (dQ, dK, dV). Use the forward's mask, scale, causal, key_len."""
     d = _desc(q)
     _same_layout(q, k, v, o, do)
     _lse_check(lse, q)
     _mask_check(block_mask, q, block_size)
+    kl = _key_len(key_len, q)
     dq = _empty_like(q) if dq is None else dq
     dk = _empty_like(q) if dk is None else dk
     dv = _empty_like(q) if dv is None else dv
@@ -188,8 +192,9 @@ def blocksparse_bwd(q, k, v, o, do, lse, block_mask, block_size, scale=None, dq=
     ws = _workspace(need, q, workspace)
     st = lib().fa_blocksparse_bwd(ctypes.byref(d), q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                                   do.data_ptr(), lse.data_ptr(), _scale(scale, q.shape[-1]),
-                                  block_mask.data_ptr(), int(block_size), dq.data_ptr(), dk.data_ptr(),
-                                  dv.data_ptr(), ws.data_ptr(), ws.numel() * ws.element_size(), _stream(q))
+                                  int(bool(causal)), _ptr(kl), block_mask.data_ptr(), int(block_size),
+                                  dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(),
+                                  ws.numel() * ws.element_size(), _stream(q))
     _check(st, "fa_blocksparse_bwd")
     return dq, dk, dv
 

@@ -59,8 +59,9 @@ def _load():
         "fa_bwd_workspace_bytes": (SZ, [DESC]),
         "fa_bwd": (ctypes.c_int, [DESC, P, P, P, P, P, P, F32, ctypes.c_int, P, P, P, P, P, SZ, P]),
         "fa_blocksparse_workspace_bytes": (SZ, [DESC, I32, ctypes.c_int]),
-        "fa_blocksparse_fwd": (ctypes.c_int, [DESC, P, P, P, F32, P, I32, P, P, P, SZ, P]),
-        "fa_blocksparse_bwd": (ctypes.c_int, [DESC, P, P, P, P, P, P, F32, P, I32, P, P, P, P, SZ, P]),
+        "fa_blocksparse_fwd": (ctypes.c_int, [DESC, P, P, P, F32, ctypes.c_int, P, P, I32, P, P, P, SZ, P]),
+        "fa_blocksparse_bwd": (ctypes.c_int, [DESC, P, P, P, P, P, P, F32, ctypes.c_int, P, P, I32, P, P, P,
+                                              P, SZ, P]),
         "fa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "fa_version": (ctypes.c_int, []),
         "fa_timer_enable": (ctypes.c_int, [ctypes.c_int]),

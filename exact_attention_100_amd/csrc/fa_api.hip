@@ -274,8 +274,9 @@ extern "C" size_t fa_blocksparse_workspace_bytes(const fa_desc* desc, int32_t bl
 }
 
 extern "C" int fa_blocksparse_fwd(const fa_desc* desc, const void* Q, const void* K, const void* V,
-                                  float scale, const uint8_t* block_mask, int32_t block_size, void* O,
-                                  float* LSE, void* workspace, size_t workspace_bytes, void* stream) {
+                                  float scale, int causal, const int32_t* key_len,
+                                  const uint8_t* block_mask, int32_t block_size, void* O, float* LSE,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
   int st = check_desc(desc);
   if (st) return st;
   if (desc->dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
@@ -287,9 +288,9 @@ extern "C" int fa_blocksparse_fwd(const fa_desc* desc, const void* Q, const void
   if (!workspace || !aligned16(workspace) || workspace_bytes < lists_bytes(nb)) return FA_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const Lists l = carve_lists(workspace, nb);
-  hipError_t e = launch_block_lists(block_mask, nb, l.row_ptr, l.col_idx, l.col_ptr, l.row_idx, s);
+  hipError_t e = launch_block_lists(block_mask, nb, causal != 0, l.row_ptr, l.col_idx, l.col_ptr, l.row_idx, s);
   if (e != hipSuccess) return FA_ERR_HIP;
-  FwdArgs a = fwd_args(desc, Q, K, V, scale, 0, nullptr, O, LSE);
+  FwdArgs a = fwd_args(desc, Q, K, V, scale, causal != 0, key_len, O, LSE);
   a.row_ptr = l.row_ptr;
   a.col_idx = l.col_idx;
   a.block_size = block_size;
@@ -297,9 +298,10 @@ extern "C" int fa_blocksparse_fwd(const fa_desc* desc, const void* Q, const void
 }
 
 extern "C" int fa_blocksparse_bwd(const fa_desc* desc, const void* Q, const void* K, const void* V,
-                                  const void* O, const void* dO, const float* LSE, float scale,
-                                  const uint8_t* block_mask, int32_t block_size, void* dQ, void* dK,
-                                  void* dV, void* workspace, size_t workspace_bytes, void* stream) {
+                                  const void* O, const void* dO, const float* LSE, float scale, int causal,
+                                  const int32_t* key_len, const uint8_t* block_mask, int32_t block_size,
+                                  void* dQ, void* dK, void* dV, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
   int st = check_desc(desc);
   if (st) return st;
   if (desc->dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
@@ -312,9 +314,9 @@ extern "C" int fa_blocksparse_bwd(const fa_desc* desc, const void* Q, const void
   if (!workspace || !aligned16(workspace) || workspace_bytes < lb + bwd_ws_bytes(desc)) return FA_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const Lists l = carve_lists(workspace, nb);
-  hipError_t e = launch_block_lists(block_mask, nb, l.row_ptr, l.col_idx, l.col_ptr, l.row_idx, s);
+  hipError_t e = launch_block_lists(block_mask, nb, causal != 0, l.row_ptr, l.col_idx, l.col_ptr, l.row_idx, s);
   if (e != hipSuccess) return FA_ERR_HIP;
-  BwdArgs a = bwd_args(desc, Q, K, V, O, dO, LSE, scale, 0, nullptr, dQ, dK, dV);
+  BwdArgs a = bwd_args(desc, Q, K, V, O, dO, LSE, scale, causal != 0, key_len, dQ, dK, dV);
   carve_bwd(desc, static_cast<char*>(workspace) + lb, a);
   a.row_ptr = l.row_ptr;
   a.col_idx = l.col_idx;

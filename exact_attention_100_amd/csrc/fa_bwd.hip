@@ -106,7 +106,9 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdKParams p) {
 // (P = 0) and such keys are masked (P = 0); their outputs are not stored.
 // VLDS: the key block's V stays in LDS (read as the B operand of dP) instead of
 // VGPRs, which keeps the d = 128 kernel within 256 registers (two waves per SIMD).
-template <int D, int BRQ, bool SPARSE, bool VLDS>
+// SMASK: a block-sparse launch that also applies the causal / key-length
+// element masks (without it, sparse tiles are never masked).
+template <int D, int BRQ, bool SPARSE, bool VLDS, bool SMASK = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FA_BWD_WAVES_PER_EU)))
 void bwd_dkdv_kernel(BwdKParams p) {
   constexpr int NQB = BRQ / 32;
@@ -146,16 +148,17 @@ void bwd_dkdv_kernel(BwdKParams p) {
   const int64_t rowbase = (int64_t)inst * N;
 
   int kv_len = N;
-  if (!SPARSE && p.key_len) kv_len = min(max(p.key_len[b], 0), N);
+  if (p.key_len) kv_len = min(max(p.key_len[b], 0), N);
 
-  // The query tiles this key block visits.
+  // The query tiles this key block visits (none when all its keys are past
+  // kv_len: dK = dV = 0).
   int n_qt, qt_begin = 0, cbeg = 0;
-  if (SPARSE) {
+  if (k0 >= kv_len) {
+    n_qt = 0;
+  } else if (SPARSE) {
     const int kbs = k0 / p.bs;
     cbeg = p.col_ptr[kbs];
     n_qt = (p.col_ptr[kbs + 1] - cbeg) * (p.bs / BRQ);
-  } else if (k0 >= kv_len) {
-    n_qt = 0;
   } else {
     qt_begin = p.causal ? k0 / BRQ : 0;
     n_qt = (N + BRQ - 1) / BRQ - qt_begin;
@@ -246,7 +249,7 @@ void bwd_dkdv_kernel(BwdKParams p) {
       // q0 + 32 sb + 8 (r/4) + 4 g + r%4. Rows past N carry lse2 = +inf (P = 0)
       // only when they exist in the loaded statistics, so they are masked too.
       const bool need_mask =
-          !SPARSE && ((p.causal && q0 < kw0 + 31) || (kw0 + 32 > kv_len) || (q0 + BRQ > N));
+          (!SPARSE || SMASK) && ((p.causal && q0 < kw0 + 31) || (kw0 + 32 > kv_len) || (q0 + BRQ > N));
       // Masked entries of S become -inf, so that 2^(c S - lse2) = 0 there (c > 0).
       if (need_mask) {
 #pragma unroll
@@ -344,7 +347,7 @@ void bwd_dkdv_kernel(BwdKParams p) {
 //                                   B = dS^T straight from the accumulator layout).
 // Loads past the end are clamped to the last row: such keys are masked (P = 0)
 // and such queries are not stored.
-template <int D, int BC, bool SPARSE>
+template <int D, int BC, bool SPARSE, bool SMASK = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FA_BWD_WAVES_PER_EU)))
 void bwd_dq_kernel(BwdKParams p) {
   constexpr int NKB = BC / 32;
@@ -379,12 +382,12 @@ void bwd_dq_kernel(BwdKParams p) {
 
   // The key tiles this query block visits (as in the forward).
   int kv_len = N, n_tiles, blk_begin = 0;
+  if (p.key_len) kv_len = min(max(p.key_len[b], 0), N);
   if (SPARSE) {
     const int rb = q0 / p.bs;
     blk_begin = p.row_ptr[rb];
     n_tiles = (p.row_ptr[rb + 1] - blk_begin) * (p.bs / BC);
   } else {
-    if (p.key_len) kv_len = min(max(p.key_len[b], 0), N);
     int kv_end = kv_len;
     if (p.causal) kv_end = min(kv_end, q0 + kBwdBlock);
     n_tiles = kv_end > 0 ? (kv_end + BC - 1) / BC : 0;
@@ -452,7 +455,7 @@ void bwd_dq_kernel(BwdKParams p) {
       }
 
     // dS^T = P^T (dP^T - D); register r of block kb is key kv0 + 32 kb + 8 (r/4) + 4 g + r%4.
-    const bool need_mask = !SPARSE && ((kv0 + BC > kv_len) || (p.causal && kv0 + BC - 1 > q0 + 32 * wave));
+    const bool need_mask = (!SPARSE || SMASK) && ((kv0 + BC > kv_len) || (p.causal && kv0 + BC - 1 > q0 + 32 * wave));
     // Masked entries of S become -inf, so that 2^(c S - lse2) = 0 there (c > 0).
     if (need_mask) {
 #pragma unroll
@@ -546,6 +549,7 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s) {
   p.bs = a.block_size;
   p.n_blocks = (a.N + kBwdBlock - 1) / kBwdBlock;
   const bool sparse = a.col_ptr != nullptr;
+  const bool smask = a.causal || a.key_len != nullptr;
   const int64_t rows = (int64_t)a.B * a.H * a.N;
   const dim3 block(256);
 
@@ -563,10 +567,12 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)(a.B * a.H * p.n_blocks));
   timer_begin("fa_bwd_dkdv", s);
   if (a.d == 128) {
-    if (sparse) bwd_dkdv_kernel<128, TQ128, true, true><<<grid, block, 0, s>>>(p);
+    if (sparse && smask) bwd_dkdv_kernel<128, TQ128, true, true, true><<<grid, block, 0, s>>>(p);
+    else if (sparse) bwd_dkdv_kernel<128, TQ128, true, true><<<grid, block, 0, s>>>(p);
     else bwd_dkdv_kernel<128, TQ128, false, true><<<grid, block, 0, s>>>(p);
   } else {
-    if (sparse) bwd_dkdv_kernel<64, TQ64, true, false><<<grid, block, 0, s>>>(p);
+    if (sparse && smask) bwd_dkdv_kernel<64, TQ64, true, false, true><<<grid, block, 0, s>>>(p);
+    else if (sparse) bwd_dkdv_kernel<64, TQ64, true, false><<<grid, block, 0, s>>>(p);
     else bwd_dkdv_kernel<64, TQ64, false, false><<<grid, block, 0, s>>>(p);
   }
   timer_end(s);
@@ -575,10 +581,12 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s) {
 
   timer_begin("fa_bwd_dq", s);
   if (a.d == 128) {
-    if (sparse) bwd_dq_kernel<128, TK128, true><<<grid, block, 0, s>>>(p);
+    if (sparse && smask) bwd_dq_kernel<128, TK128, true, true><<<grid, block, 0, s>>>(p);
+    else if (sparse) bwd_dq_kernel<128, TK128, true><<<grid, block, 0, s>>>(p);
     else bwd_dq_kernel<128, TK128, false><<<grid, block, 0, s>>>(p);
   } else {
-    if (sparse) bwd_dq_kernel<64, TK64, true><<<grid, block, 0, s>>>(p);
+    if (sparse && smask) bwd_dq_kernel<64, TK64, true, true><<<grid, block, 0, s>>>(p);
+    else if (sparse) bwd_dq_kernel<64, TK64, true><<<grid, block, 0, s>>>(p);
     else bwd_dq_kernel<64, TK64, false><<<grid, block, 0, s>>>(p);
   }
   timer_end(s);
@@ -587,56 +595,148 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s) {
 
 // ------------------------------------------------------------------------------ block lists
 
-// One workgroup: per-row (CSR) and per-column (CSC) lists of the nonzero blocks
-// of an nb x nb mask (nb <= 1024), indices in increasing order.
-__global__ __launch_bounds__(1024) void block_lists_kernel(const uint8_t* mask, int nb, int32_t* row_ptr,
-                                                           int32_t* col_idx, int32_t* col_ptr,
-                                                           int32_t* row_idx) {
-  __shared__ int32_t rcount[1024], ccount[1024], rstart[1025], cstart[1025];
-  const int tid = threadIdx.x;
-  for (int i = tid; i < nb; i += 1024) {
-    int rc = 0, cc = 0;
-    for (int j = 0; j < nb; ++j) {
-      rc += mask[(int64_t)i * nb + j] != 0;
-      cc += mask[(int64_t)j * nb + i] != 0;
-    }
-    rcount[i] = rc;
-    ccount[i] = cc;
+// One workgroup: per-row (CSR) and per-column (CSC) lists of the kept blocks of
+// an nb x nb mask (nb <= 1024), indices in increasing order. With causal,
+// blocks above the diagonal (key block > query block) are dropped: every
+// element of them is masked. STAGED: the mask (nb * nb <= kStagedMask bytes)
+// is first copied into LDS, so the scans below read LDS instead of making
+// long chains of dependent global loads.
+constexpr int kStagedMask = 65536;
+
+// Exclusive prefix sum of v over the 1024 threads of the workgroup (thread i
+// holds element i); returns element i's prefix, and the total in *total.
+__device__ __forceinline__ int block_exclusive_scan(int v, int32_t* wsum, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wsum[wave] = x;
+  __syncthreads();
+  int before = 0, all = 0;
+  for (int w = 0; w < 16; ++w) {
+    const int s = wsum[w];
+    before += w < wave ? s : 0;
+    all += s;
   }
   __syncthreads();
+  *total = all;
+  return before + x - v;
+}
+
+template <bool STAGED>
+__global__ __launch_bounds__(1024) void block_lists_kernel(const uint8_t* mask, int nb, int causal,
+                                                           int32_t* row_ptr, int32_t* col_idx,
+                                                           int32_t* col_ptr, int32_t* row_idx) {
+  __shared__ int32_t rcount[1024], ccount[1024], rstart[1024], cstart[1024], wsum[16];
+  __shared__ int32_t cpart[1024];  // per (row slice, column) counts, then their offsets
+  __shared__ __attribute__((aligned(16))) uint8_t smask[STAGED ? kStagedMask : 4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;  // 16 waves
+  const int total = nb * nb;
+  if (STAGED && (total & 3) == 0 && ((uintptr_t)mask & 3) == 0) {
+    // Dword copies (at most 16 per thread), all issued before the first store.
+    const int words = total >> 2;
+    const uint32_t* m32 = reinterpret_cast<const uint32_t*>(mask);
+    uint32_t* s32 = reinterpret_cast<uint32_t*>(smask);
+    for (int i0 = 0; i0 < words; i0 += 1024 * 4) {
+      uint32_t v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = m32[min(i0 + u * 1024 + tid, words - 1)];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (i0 + u * 1024 + tid < words) s32[i0 + u * 1024 + tid] = v[u];
+    }
+    __syncthreads();
+  } else if (STAGED) {
+    for (int i0 = 0; i0 < total; i0 += 1024 * 8) {
+      uint8_t v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = mask[min(i0 + u * 1024 + tid, total - 1)];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = i0 + u * 1024 + tid;
+        if (i < total) smask[i] = v[u];
+      }
+    }
+    __syncthreads();
+  }
+  auto keep = [&](int r, int c) -> bool {
+    const uint8_t m = STAGED ? smask[r * nb + c] : mask[(int64_t)r * nb + c];
+    return m != 0 && (!causal || c <= r);
+  };
+  // Row counts: one wave per row, 64 consecutive columns per step (ballot).
+  // Column counts: thread (slice, c) walks column c over its slice of the rows,
+  // so that a wave reads consecutive bytes per step (reading a column across the
+  // lanes of a wave would put them all on one LDS bank) and every thread works.
+  const int nsl = nb >= 1024 ? 1 : 1024 / nb;        // row slices per column
+  const int rows_sl = (nb + nsl - 1) / nsl;          // rows per slice
+  const int sl = tid / nb, col = tid - sl * nb;      // this thread's (slice, column)
+  const bool has_col = sl < nsl;
+  const int r_lo = min(sl * rows_sl, nb), r_hi = min(r_lo + rows_sl, nb);
+  for (int i = wave; i < nb; i += 16) {
+    int rc = 0;
+    for (int j0 = 0; j0 < nb; j0 += 64) rc += __popcll(__ballot(j0 + lane < nb && keep(i, j0 + lane)));
+    if (lane == 0) rcount[i] = rc;
+  }
+  if (has_col) {
+    int cc = 0;
+    for (int r = r_lo; r < r_hi; ++r) cc += keep(r, col);
+    cpart[tid] = cc;
+  }
+  __syncthreads();
+  // Column totals, and each slice's offset within its column (in place).
+  if (tid < nb) {
+    int acc = 0;
+    for (int s = 0; s < nsl; ++s) {
+      const int c = cpart[s * nb + tid];
+      cpart[s * nb + tid] = acc;
+      acc += c;
+    }
+    ccount[tid] = acc;
+  }
+  __syncthreads();
+  int rtot, ctot;
+  const int rs = block_exclusive_scan(tid < nb ? rcount[tid] : 0, wsum, &rtot);
+  const int cs = block_exclusive_scan(tid < nb ? ccount[tid] : 0, wsum, &ctot);
+  if (tid < nb) {
+    rstart[tid] = rs;
+    cstart[tid] = cs;
+    row_ptr[tid] = rs;
+    col_ptr[tid] = cs;
+  }
   if (tid == 0) {
-    int acc = 0;
-    for (int i = 0; i < nb; ++i) {
-      rstart[i] = acc;
-      acc += rcount[i];
-    }
-    rstart[nb] = acc;
-  } else if (tid == 64) {
-    int acc = 0;
-    for (int i = 0; i < nb; ++i) {
-      cstart[i] = acc;
-      acc += ccount[i];
-    }
-    cstart[nb] = acc;
+    row_ptr[nb] = rtot;
+    col_ptr[nb] = ctot;
   }
   __syncthreads();
-  for (int i = tid; i <= nb; i += 1024) {
-    row_ptr[i] = rstart[i];
-    col_ptr[i] = cstart[i];
-  }
-  for (int i = tid; i < nb; i += 1024) {
-    int rp = rstart[i], cp = cstart[i];
-    for (int j = 0; j < nb; ++j) {
-      if (mask[(int64_t)i * nb + j] != 0) col_idx[rp++] = j;
-      if (mask[(int64_t)j * nb + i] != 0) row_idx[cp++] = j;
+  // The lists, in increasing index order. Columns of a row: one wave per row, a
+  // kept entry's slot being the number of kept entries before it (ballot prefix
+  // count). Rows of a column: one thread per column, as for the counts.
+  for (int i = wave; i < nb; i += 16) {
+    int rb = rstart[i];
+    for (int j0 = 0; j0 < nb; j0 += 64) {
+      const bool kr = j0 + lane < nb && keep(i, j0 + lane);
+      const uint64_t br = __ballot(kr);
+      if (kr) col_idx[rb + __popcll(br & ((1ull << lane) - 1ull))] = j0 + lane;
+      rb += __popcll(br);
     }
+  }
+  if (has_col) {
+    int cp = cstart[col] + cpart[tid];
+    for (int r = r_lo; r < r_hi; ++r)
+      if (keep(r, col)) row_idx[cp++] = r;
   }
 }
 
-hipError_t launch_block_lists(const uint8_t* mask, int nb, int32_t* row_ptr, int32_t* col_idx,
+hipError_t launch_block_lists(const uint8_t* mask, int nb, int causal, int32_t* row_ptr, int32_t* col_idx,
                               int32_t* col_ptr, int32_t* row_idx, hipStream_t s) {
   timer_begin("fa_block_lists", s);
-  block_lists_kernel<<<dim3(1), dim3(1024), 0, s>>>(mask, nb, row_ptr, col_idx, col_ptr, row_idx);
+  if (nb * nb <= kStagedMask)
+    block_lists_kernel<true><<<dim3(1), dim3(1024), 0, s>>>(mask, nb, causal, row_ptr, col_idx, col_ptr, row_idx);
+  else
+    block_lists_kernel<false><<<dim3(1), dim3(1024), 0, s>>>(mask, nb, causal, row_ptr, col_idx, col_ptr, row_idx);
   timer_end(s);
   return hipGetLastError();
 }

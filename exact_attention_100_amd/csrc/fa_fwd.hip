@@ -58,12 +58,14 @@ __device__ __forceinline__ FwdRange fwd_range(const FwdKParams& p, int b, int q0
   FwdRange r;
   r.kv_len = p.N;
   r.blk_begin = 0;
+  if (p.key_len) r.kv_len = min(max(p.key_len[b], 0), p.N);
   if (SPARSE) {
+    // The row's kept blocks (blocks above the diagonal are already dropped from
+    // the lists when causal); key_len and the diagonal blocks mask per element.
     const int rb = q0 / p.bs;
     r.blk_begin = p.row_ptr[rb];
     r.n_tiles = (p.row_ptr[rb + 1] - r.blk_begin) * (p.bs / BC);
   } else {
-    if (p.key_len) r.kv_len = min(max(p.key_len[b], 0), p.N);
     int kv_end = r.kv_len;
     if (p.causal) kv_end = min(kv_end, q0 + kFwdRows);
     r.n_tiles = kv_end > 0 ? (kv_end + BC - 1) / BC : 0;
@@ -188,7 +190,9 @@ __device__ __forceinline__ float softmax_tile_bf16(f32x16 (&s)[NKB], float c, fl
 #define FA_FWD_WAVES_PER_EU 2
 #endif
 
-template <int D, int BC, bool SPARSE>
+// SMASK: a block-sparse launch that also applies the causal / key-length
+// element masks (without it, sparse tiles are never masked).
+template <int D, int BC, bool SPARSE, bool SMASK = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FA_FWD_WAVES_PER_EU)))
 void fwd_bf16_kernel(FwdKParams p) {
   constexpr int NKB = BC / 32;
@@ -286,7 +290,7 @@ void fwd_bf16_kernel(FwdKParams p) {
       for (int db = 0; db < NDB; ++db) oacc[db] = mfma_bf16(to.read_tr(sv, ks, db), pb[ks], oacc[db]);
   };
   auto needs_mask = [&](int kv0) {
-    return !SPARSE && ((kv0 + BC > rg.kv_len) || (p.causal && kv0 + BC - 1 > q0 + wave * 32));
+    return (!SPARSE || SMASK) && ((kv0 + BC > rg.kv_len) || (p.causal && kv0 + BC - 1 > q0 + wave * 32));
   };
 
   if (nt > 0) {
@@ -575,13 +579,16 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s) {
   const FwdKParams p = make_params(a);
   const dim3 grid((unsigned)(a.B * a.H * p.n_qblocks)), block(256);
   const bool sparse = a.row_ptr != nullptr;
+  const bool smask = a.causal || a.key_len != nullptr;
   timer_begin("fa_fwd_bf16", s);
   constexpr int BC128 = FA_FWD_BC_D128, BC64 = FA_FWD_BC_D64, BCS64 = FA_FWD_BC_SPARSE_D64;
   if (a.d == 128) {
-    if (sparse) fwd_bf16_kernel<128, BC128, true><<<grid, block, 0, s>>>(p);
+    if (sparse && smask) fwd_bf16_kernel<128, BC128, true, true><<<grid, block, 0, s>>>(p);
+    else if (sparse) fwd_bf16_kernel<128, BC128, true><<<grid, block, 0, s>>>(p);
     else fwd_bf16_kernel<128, BC128, false><<<grid, block, 0, s>>>(p);
   } else {
-    if (sparse) fwd_bf16_kernel<64, BCS64, true><<<grid, block, 0, s>>>(p);
+    if (sparse && smask) fwd_bf16_kernel<64, BCS64, true, true><<<grid, block, 0, s>>>(p);
+    else if (sparse) fwd_bf16_kernel<64, BCS64, true><<<grid, block, 0, s>>>(p);
     else fwd_bf16_kernel<64, BC64, false><<<grid, block, 0, s>>>(p);
   }
   timer_end(s);

@@ -58,8 +58,9 @@ void timer_end(hipStream_t stream);
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s);
-// Builds row_ptr[nb+1], col_idx[nb*nb], col_ptr[nb+1], row_idx[nb*nb] from the mask.
-hipError_t launch_block_lists(const uint8_t* mask, int nb, int32_t* row_ptr, int32_t* col_idx,
+// Builds row_ptr[nb+1], col_idx[nb*nb], col_ptr[nb+1], row_idx[nb*nb] from the mask
+// (blocks above the diagonal dropped when causal).
+hipError_t launch_block_lists(const uint8_t* mask, int nb, int causal, int32_t* row_ptr, int32_t* col_idx,
                               int32_t* col_ptr, int32_t* row_idx, hipStream_t s);
 
 }  // namespace fa

@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define FA_VERSION 100
+#define FA_VERSION 101
 
 enum fa_status {
   FA_OK = 0,
@@ -106,18 +106,24 @@ size_t fa_blocksparse_workspace_bytes(const fa_desc* desc, int32_t block_size, i
 /* Block-sparse forward: fa_fwd restricted to the nonzero blocks of
  * `block_mask` (device uint8 [N/bs][N/bs], row = query block, shared over B
  * and H); zero blocks are never loaded or computed (reading notes,
- * §Introduction › Block-sparse FlashAttention). Requires N % bs == 0 and bs a
- * positive multiple of 128. No causal or key_len. bf16 only. */
+ * §Introduction › Block-sparse FlashAttention). `causal` and `key_len` (as in
+ * fa_fwd, may be 0 / NULL) combine with the block mask by AND: an entry is kept
+ * iff its block is nonzero, and it is causal-allowed, and its key is below the
+ * batch's key length. Blocks above the diagonal are then skipped when causal.
+ * Requires N % bs == 0 and bs a positive multiple of 128. bf16 only. */
 int fa_blocksparse_fwd(const fa_desc* desc, const void* Q, const void* K, const void* V,
-                       float scale, const uint8_t* block_mask, int32_t block_size, void* O,
-                       float* LSE, void* workspace, size_t workspace_bytes, void* stream);
+                       float scale, int causal, const int32_t* key_len,
+                       const uint8_t* block_mask, int32_t block_size, void* O, float* LSE,
+                       void* workspace, size_t workspace_bytes, void* stream);
 
-/* Block-sparse backward: fa_bwd restricted to the nonzero blocks; needs the O
- * and LSE of fa_blocksparse_fwd with the same mask. Same requirements. */
+/* Block-sparse backward: fa_bwd restricted to the kept blocks; needs the O and
+ * LSE of fa_blocksparse_fwd with the same mask, causal flag and key lengths.
+ * Same requirements. */
 int fa_blocksparse_bwd(const fa_desc* desc, const void* Q, const void* K, const void* V,
-                       const void* O, const void* dO, const float* LSE, float scale,
-                       const uint8_t* block_mask, int32_t block_size, void* dQ, void* dK,
-                       void* dV, void* workspace, size_t workspace_bytes, void* stream);
+                       const void* O, const void* dO, const float* LSE, float scale, int causal,
+                       const int32_t* key_len, const uint8_t* block_mask, int32_t block_size,
+                       void* dQ, void* dK, void* dV, void* workspace, size_t workspace_bytes,
+                       void* stream);
 
 /* Static, human-readable name of a status code. */
 const char* fa_status_string(int status);

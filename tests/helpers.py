@@ -55,14 +55,16 @@ def run_gpu(case: workloads.Case, backward: bool = True):
     t = upload(case)
     sc = float(case.scale)
     if case.block_mask is not None:
-        o, lse = fa.blocksparse_fwd(t["q"], t["k"], t["v"], t["block_mask"], case.block_size, scale=sc)
+        o, lse = fa.blocksparse_fwd(t["q"], t["k"], t["v"], t["block_mask"], case.block_size, scale=sc,
+                                    causal=case.causal, key_len=t["key_len"])
     else:
         o, lse = fa.fwd(t["q"], t["k"], t["v"], scale=sc, causal=case.causal, key_len=t["key_len"])
     out = {"o": o, "lse": lse}
     if backward:
         if case.block_mask is not None:
             dq, dk, dv = fa.blocksparse_bwd(t["q"], t["k"], t["v"], o, t["do"], lse, t["block_mask"],
-                                            case.block_size, scale=sc)
+                                            case.block_size, scale=sc, causal=case.causal,
+                                            key_len=t["key_len"])
         else:
             dq, dk, dv = fa.bwd(t["q"], t["k"], t["v"], o, t["do"], lse, scale=sc, causal=case.causal,
                                 key_len=t["key_len"])

@@ -37,7 +37,7 @@ def test_library_exports_every_header_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.fa_version() == 100
+    assert lib.fa_version() == 101
     for code in (0, -1, -2, -3, -4):
         assert lib.fa_status_string(code)
     assert b"unknown" in lib.fa_status_string(7)
@@ -72,9 +72,9 @@ def test_argument_errors_before_any_launch(lib):
     assert lib.fa_bwd(ref(d), A, A, A, A, A, A, 0.1, 0, None, A, A, A, None, need, None) == -3
     # block-sparse: block size must be a multiple of 128 that divides N
     for bs in (64, 100, 192, 512):
-        assert lib.fa_blocksparse_fwd(ref(d), A, A, A, 0.1, A, bs, A, A, A, 1 << 30, None) == -1
-    assert lib.fa_blocksparse_fwd(ref(d), A, A, A, 0.1, None, 128, A, A, A, 1 << 30, None) == -1
-    assert lib.fa_blocksparse_fwd(ref(d), A, A, A, 0.1, A, 128, A, A, A, 16, None) == -3
+        assert lib.fa_blocksparse_fwd(ref(d), A, A, A, 0.1, 0, None, A, bs, A, A, A, 1 << 30, None) == -1
+    assert lib.fa_blocksparse_fwd(ref(d), A, A, A, 0.1, 0, None, None, 128, A, A, A, 1 << 30, None) == -1
+    assert lib.fa_blocksparse_fwd(ref(d), A, A, A, 0.1, 1, None, A, 128, A, A, A, 16, None) == -3
     assert lib.fa_blocksparse_workspace_bytes(ref(d), 100, 0) == 0
 
 

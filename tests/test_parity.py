@@ -192,6 +192,33 @@ def test_block_sparse_masks(kind, d, bs):
         assert np.all(gpu["dk"][:, :, 2 * bs:3 * bs] == 0) and np.all(gpu["dv"][:, :, 2 * bs:3 * bs] == 0)
 
 
+@pytest.mark.parametrize("mask", ["block+causal", "block+key_len", "block+causal+key_len"])
+@pytest.mark.parametrize("d,bs", [(64, 128), (128, 128), (64, 256)])
+def test_block_sparse_combined_with_causal_and_key_len(mask, d, bs):
+    """The block mask ANDed with the causal and key-length masks (blocks above the diagonal
+    skipped, diagonal and key-length blocks masked per element)."""
+    N = 4 * bs
+    case = workloads.make_case(2, 2, N, d, mask=mask, block_size=bs, block_p=0.5, seed=18,
+                               key_len_range=(bs // 2, N - 1), name=f"combined-{mask}")
+    case.block_mask[2, 0] = 1  # at least one kept block below the diagonal
+    _check_case(case)
+
+
+def test_block_sparse_causal_all_ones_equals_dense_causal_kernel():
+    import torch
+    import exact_attention_100_amd as fa
+    case = workloads.make_case(2, 2, 512, 128, mask="causal", seed=19, name="sparse-causal-vs-dense")
+    _say(case.name)
+    t = upload(case)
+    ones = torch.ones((4, 4), dtype=torch.uint8, device="cuda")
+    kl = torch.tensor([300, 512], dtype=torch.int32, device="cuda")
+    o1, l1 = fa.fwd(t["q"], t["k"], t["v"], causal=True, key_len=kl)
+    o2, l2 = fa.blocksparse_fwd(t["q"], t["k"], t["v"], ones, 128, causal=True, key_len=kl)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1[torch.isfinite(l1)], l2[torch.isfinite(l2)])
+    assert torch.equal(torch.isfinite(l1), torch.isfinite(l2))
+
+
 def test_block_sparse_all_ones_equals_dense_kernel():
     import torch
     import exact_attention_100_amd as fa

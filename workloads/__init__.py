@@ -111,26 +111,30 @@ def make_case(B: int, H: int, N: int, d: int, dtype: str = BF16, mask: str = "no
               key_len_range: Optional[tuple[int, int]] = None, block_size: Optional[int] = None,
               block_p: Optional[float] = None, scale: Optional[float] = None, name: str = "custom",
               std: float = 1.0) -> Case:
-    """Draw one case following the module recipe. mask in {none, causal, key_len, block}."""
+    """Draw one case following the module recipe. mask: "none", or kinds from {causal, key_len,
+    block} joined by "+" (e.g. "block+causal"); the draws happen in the order Q, K, V, dO, key
+    lengths, block mask whatever the order of the kinds."""
+    kinds = set() if mask == "none" else set(mask.split("+"))
+    assert kinds <= {"causal", "key_len", "block"}, mask
     rng = np.random.default_rng(seed)
     shape = (B, H, N, d)
     arrs = [rng.standard_normal(shape, dtype=np.float32) for _ in range(4)]
     if std != 1.0:
         arrs = [a * np.float32(std) for a in arrs]
     key_len = None
-    if mask == "key_len":
+    if "key_len" in kinds:
         lo, hi = key_len_range if key_len_range is not None else (0, N)
         key_len = rng.integers(lo, hi + 1, size=B).astype(np.int32)
     block_mask = None
-    if mask == "block":
+    if "block" in kinds:
         assert block_size is not None and N % block_size == 0
         block_mask = draw_block_mask(rng, N // block_size, 0.125 if block_p is None else block_p)
     if dtype == BF16:
         arrs = [bf16_round(a) for a in arrs]
     sc = np.float32(1.0 / np.sqrt(d)) if scale is None else np.float32(scale)
-    return Case(name=name, B=B, H=H, N=N, d=d, dtype=dtype, causal=(mask == "causal"), scale=sc,
+    return Case(name=name, B=B, H=H, N=N, d=d, dtype=dtype, causal="causal" in kinds, scale=sc,
                 q=arrs[0], k=arrs[1], v=arrs[2], do=arrs[3], key_len=key_len, block_mask=block_mask,
-                block_size=block_size if mask == "block" else None, seed=seed)
+                block_size=block_size if "block" in kinds else None, seed=seed)
 
 
 def make_config(name: str, seed: Optional[int] = None) -> Case:
