@@ -31,6 +31,11 @@ three equations above (the pages defer it to the paper's appendix):
   dS = P o (dP - D 1^T),  dQ = scale * dS K,  dK = scale * dS^T Q.
 It recomputes P from Q and K; it never uses any LSE produced elsewhere.
 
+forward_rows, backward_rows and backward_keys evaluate the same equations for
+chosen query rows / key columns of one instance, a chunk of rows at a time and
+only over the keys each chunk may attend, so that long sequences never need the
+N x N matrices; they are pinned against forward() / backward().
+
 Pins (tests/test_oracle.py): hand-solved N=2 and N=4 cases (tests/golden/),
 row sums, closed forms (scale 0, N 1, causal row 0), reductions of every mask
 to plain attention on a sub-range, shift invariances, central finite
@@ -46,11 +51,12 @@ import numpy as np
 
 def allowed_matrix(N: int, causal: bool = False, key_len: Optional[int] = None,
                    block_mask: Optional[np.ndarray] = None, block_size: Optional[int] = None,
-                   rows: Optional[np.ndarray] = None) -> np.ndarray:
-    """Boolean [len(rows), N]: entry (i, j) is True iff key j may be attended by query rows[i]."""
+                   rows: Optional[np.ndarray] = None, cols: Optional[np.ndarray] = None) -> np.ndarray:
+    """Boolean [len(rows), len(cols)] (all rows / keys by default): entry (i, j) is True iff
+    key cols[j] may be attended by query rows[i]."""
     r = np.arange(N) if rows is None else np.asarray(rows)
-    j = np.arange(N)
-    ok = np.ones((r.size, N), dtype=bool)
+    j = np.arange(N) if cols is None else np.asarray(cols)
+    ok = np.ones((r.size, j.size), dtype=bool)
     if causal:
         ok &= j[None, :] <= r[:, None]
     if key_len is not None:
@@ -130,6 +136,97 @@ def forward_rows(Q, K, V, scale, b, h, rows, causal=False, key_len=None, block_m
     L = None if key_len is None else int(key_len[b])
     ok = allowed_matrix(N, causal, L, block_mask, block_size, rows=rows)
     return head_forward(_f64(Q[b, h][rows]), _f64(K[b, h]), _f64(V[b, h]), scale, ok)
+
+
+# ----------------------------------------------------------------------------- sampled evaluation
+#
+# For long sequences the N x N matrices do not fit. The functions below evaluate
+# the same equations for chosen query rows or key columns of one (b, h) instance,
+# a chunk of query rows at a time. Each chunk only touches the union of the keys
+# its rows may attend (masked keys contribute exp(-inf) = 0 to every sum), so a
+# causal or block-sparse instance costs what its kept pairs cost. They are pinned
+# against forward() / backward() on sizes where those fit (tests/test_oracle.py).
+
+
+def _candidate_cols(N, rows, L, causal, block_mask, block_size):
+    """A superset of the keys that query rows `rows` may attend: below the causal and key-length
+    bounds, and inside the key blocks that the rows' query blocks keep."""
+    hi = N
+    if causal:
+        hi = min(hi, int(np.max(rows)) + 1)
+    if L is not None:
+        hi = min(hi, max(int(L), 0))
+    if block_mask is None:
+        return np.arange(hi)
+    bs = int(block_size)
+    kept = np.nonzero(np.asarray(block_mask)[np.unique(np.asarray(rows) // bs)].any(axis=0))[0]
+    c = (kept[:, None] * bs + np.arange(bs)[None, :]).ravel()
+    return c[c < hi]
+
+
+def _chunk_terms(Q, K, V, dO, scale, rows, L, causal, block_mask, block_size):
+    """For query rows `rows` of one instance: the kept key columns `cols`, and on them
+    P, dP (rows x cols), LSE and D = sum_j P_ij dP_ij per row (same equations as
+    head_probabilities / head_backward)."""
+    N = K.shape[0]
+    cand = _candidate_cols(N, rows, L, causal, block_mask, block_size)
+    ok = allowed_matrix(N, causal, L, block_mask, block_size, rows=rows, cols=cand)
+    keep = ok.any(axis=0)
+    cols, ok = cand[keep], ok[:, keep]
+    if cols.size == 0:  # no row of the chunk has a key: P = 0, LSE = -inf
+        z = np.zeros((len(rows), 0))
+        return cols, z, z, np.full(len(rows), -np.inf), np.zeros(len(rows))
+    q = _f64(Q[rows])
+    _, p, lse = head_probabilities(q, _f64(K[cols]), scale, ok)
+    dp = _f64(dO[rows]) @ _f64(V[cols]).T
+    dsum = (p * dp).sum(axis=1)
+    return cols, p, dp, lse, dsum
+
+
+def backward_rows(Q, K, V, dO, scale, b, h, rows, causal=False, key_len=None, block_mask=None,
+                  block_size=None, chunk=256):
+    """dQ of the given query rows of instance (b, h): dQ_i = scale * sum_j dS_ij K_j with
+    dS_ij = P_ij (dP_ij - D_i); each row depends only on its own P and dP."""
+    rows = np.asarray(rows)
+    L = None if key_len is None else int(key_len[b])
+    q_, k_, v_, do_ = Q[b, h], K[b, h], V[b, h], dO[b, h]
+    dq = np.zeros((rows.size, Q.shape[-1]))
+    for c0 in range(0, rows.size, chunk):
+        r = rows[c0:c0 + chunk]
+        cols, p, dp, _, dsum = _chunk_terms(q_, k_, v_, do_, scale, r, L, causal, block_mask, block_size)
+        ds = p * (dp - dsum[:, None])
+        dq[c0:c0 + chunk] = float(scale) * (ds @ _f64(k_[cols]))
+    return dq
+
+
+def backward_keys(Q, K, V, dO, scale, b, h, keys, causal=False, key_len=None, block_mask=None,
+                  block_size=None, chunk=256):
+    """dK and dV of the given keys of instance (b, h): dV_j = sum_i P_ij dO_i and
+    dK_j = scale * sum_i dS_ij Q_i over every query row i, whose LSE and D come from the
+    same chunked evaluation (rows that attend none of the keys are skipped)."""
+    keys = np.asarray(keys)
+    N, d = Q.shape[2], Q.shape[3]
+    L = None if key_len is None else int(key_len[b])
+    q_, k_, v_, do_ = Q[b, h], K[b, h], V[b, h], dO[b, h]
+    sees = allowed_matrix(N, causal, L, block_mask, block_size, cols=keys)  # [N, len(keys)]
+    dk = np.zeros((keys.size, d))
+    dv = np.zeros((keys.size, d))
+    for r0 in range(0, N, chunk):
+        r = np.arange(r0, min(r0 + chunk, N))
+        ok_k = sees[r]
+        if not ok_k.any():
+            continue
+        cols, p, dp, lse, dsum = _chunk_terms(q_, k_, v_, do_, scale, r, L, causal, block_mask, block_size)
+        # the chosen keys' columns of P and dP (zero where a key is not kept for a row)
+        s_k = float(scale) * (_f64(q_[r]) @ _f64(k_[keys]).T)
+        with np.errstate(invalid="ignore"):
+            p_k = np.where(ok_k, np.exp(np.where(ok_k, s_k, 0.0) - np.where(np.isfinite(lse), lse, 0.0)[:, None]),
+                           0.0)
+        dp_k = _f64(do_[r]) @ _f64(v_[keys]).T
+        ds_k = p_k * (dp_k - dsum[:, None])
+        dv += p_k.T @ _f64(do_[r])
+        dk += float(scale) * (ds_k.T @ _f64(q_[r]))
+    return dk, dv
 
 
 def backward(Q, K, V, dO, scale, causal=False, key_len=None, block_mask=None, block_size=None,

@@ -342,3 +342,38 @@ def test_matches_torch_sdpa_float64(mi):
     with np.errstate(divide="ignore"):
         ref_lse = np.log(np.exp(s).sum(axis=-1))
     np.testing.assert_allclose(LSE[hb[..., 0]], ref_lse[hb[..., 0]], rtol=0, atol=1e-12)
+
+
+# --------------------------------------------------------------------------- sampled evaluation
+
+SAMPLED_MASKS = MASKS + [dict(causal=True, key_len=np.array([40, 17]),
+                              block_mask=(np.random.default_rng(7).random((12, 12)) < 0.4).astype(np.uint8),
+                              block_size=5)]
+
+
+@pytest.mark.parametrize("mi", range(len(SAMPLED_MASKS)))
+def test_sampled_rows_and_keys_match_full_oracle(mi):
+    """forward_rows / backward_rows / backward_keys (chunked, restricted to the keys each chunk
+    may attend) reproduce forward() / backward() on every row and key, chunks smaller than N."""
+    kw = SAMPLED_MASKS[mi]
+    N = kw["block_mask"].shape[0] * kw["block_size"] if "block_mask" in kw else 12
+    rng = np.random.default_rng(70 + mi)
+    B, H, d = 2, 2, 8
+    q, k, v, do = (_rand(rng, B, H, N, d) for _ in range(4))
+    sc = 0.41
+    O, LSE = oracle.forward(q, k, v, sc, **kw)
+    dQ, dK, dV = oracle.backward(q, k, v, do, sc, **kw)
+    rows = np.arange(N)
+    for b in range(B):
+        for h in range(H):
+            o, lse = oracle.forward_rows(q, k, v, sc, b, h, rows, **kw)
+            np.testing.assert_allclose(o, O[b, h], rtol=0, atol=1e-12)
+            np.testing.assert_array_equal(np.isneginf(lse), np.isneginf(LSE[b, h]))
+            fin = np.isfinite(lse)
+            np.testing.assert_allclose(lse[fin], LSE[b, h][fin], rtol=0, atol=1e-12)
+            dq = oracle.backward_rows(q, k, v, do, sc, b, h, rows, chunk=5, **kw)
+            np.testing.assert_allclose(dq, dQ[b, h], rtol=0, atol=1e-12)
+            keys = rng.permutation(N)[: N // 2]
+            dk, dv = oracle.backward_keys(q, k, v, do, sc, b, h, keys, chunk=7, **kw)
+            np.testing.assert_allclose(dk, dK[b, h][keys], rtol=0, atol=1e-12)
+            np.testing.assert_allclose(dv, dV[b, h][keys], rtol=0, atol=1e-12)
