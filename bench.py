@@ -34,18 +34,24 @@ def kept_pairs(case) -> int:
     """Number of (query, key) pairs the masks keep, summed over all instances."""
     import numpy as np
     B, H, N = case.B, case.H, case.N
-    if case.block_mask is not None:
-        return int(case.block_mask.astype(np.int64).sum()) * case.block_size ** 2 * B * H
-    per_b = []
+    i = np.arange(N, dtype=np.int64)
+    total = 0
     for b in range(B):
         L = N if case.key_len is None else int(min(max(case.key_len[b], 0), N))
-        if case.causal:
-            # sum over rows i of min(i + 1, L)
-            i = np.arange(N, dtype=np.int64)
-            per_b.append(int(np.minimum(i + 1, L).sum()))
-        else:
-            per_b.append(N * L)
-    return int(sum(per_b)) * H
+        if case.block_mask is None:
+            hi = np.full(N, L, dtype=np.int64)
+            if case.causal:
+                hi = np.minimum(hi, i + 1)  # row i keeps keys j < min(i + 1, L)
+            total += int(hi.sum())
+            continue
+        bs = case.block_size
+        for rb, cb in zip(*np.nonzero(case.block_mask)):
+            rows = i[rb * bs:(rb + 1) * bs]
+            hi = np.full(bs, min(cb * bs + bs, L), dtype=np.int64)
+            if case.causal:
+                hi = np.minimum(hi, rows + 1)
+            total += int(np.maximum(hi - cb * bs, 0).sum())  # keys cb*bs <= j < hi of each row
+    return total * H
 
 
 def sources_hash() -> str:

@@ -43,6 +43,11 @@ CONFIGS: dict[str, dict] = {
                 desc="long-sequence causal, N=8192"),
     "C5": dict(B=1, H=8, N=16384, d=64, dtype=BF16, mask="block", block_size=128, block_p=0.125,
                seed=6, desc="block-sparse, 128x128 blocks, diagonal + symmetric p=1/8"),
+    # Long sequences (the pages' 64K-token tasks): measured, and parity-tested on sampled rows.
+    "L64K": dict(B=1, H=16, N=65536, d=64, dtype=BF16, mask="causal", seed=7,
+                 desc="long-sequence causal, N=65536"),
+    "L64Ks": dict(B=1, H=16, N=65536, d=64, dtype=BF16, mask="block", block_size=256, block_p=0.125,
+                  seed=8, desc="long-sequence block-sparse, N=65536, 256x256 blocks, p=1/8"),
 }
 
 
