@@ -31,6 +31,11 @@ three equations above (the pages defer it to the paper's appendix):
   dS = P o (dP - D 1^T),  dQ = scale * dS K,  dK = scale * dS^T Q.
 It recomputes P from Q and K; it never uses any LSE produced elsewhere.
 
+Dropout (the notes' list of fused steps puts dropout after the softmax): with keep
+bits Z from dropout_keep (Philox4x32-10, oracle/philox.py) and drop probability p,
+O = (P o Z) V / (1 - p) and LSE stays that of the softmax; the backward is the
+chain rule through that product (head_backward).
+
 forward_rows, backward_rows and backward_keys evaluate the same equations for
 chosen query rows / key columns of one instance, a chunk of rows at a time and
 only over the keys each chunk may attend, so that long sequences never need the
@@ -47,6 +52,8 @@ from __future__ import annotations
 from typing import Iterable, Optional
 
 import numpy as np
+
+from .philox import philox4x32
 
 
 def allowed_matrix(N: int, causal: bool = False, key_len: Optional[int] = None,
@@ -83,22 +90,61 @@ def head_probabilities(q: np.ndarray, k: np.ndarray, scale: float, allowed: np.n
     return s, p, lse
 
 
-def head_forward(q, k, v, scale, allowed):
-    """O and LSE for one head: O = P V."""
+def dropout_keep(rows, cols, bh: int, p8: int, seed: int, offset: int) -> np.ndarray:
+    """Dropout keep bits, Boolean [len(rows), len(cols)], of instance bh = b * H + h.
+
+    The pair (i, j) takes byte (j mod 4) of word (i mod 4) of Philox4x32-10 at counter
+    (i div 4, j div 4, bh, offset) with key (seed mod 2^32, seed div 2^32); it is kept iff
+    that byte is >= p8 (the drop probability is p8 / 256)."""
+    r = np.asarray(rows, dtype=np.int64)[:, None]
+    c = np.asarray(cols, dtype=np.int64)[None, :]
+    shape = np.broadcast_shapes(r.shape, c.shape)
+    ctr = np.stack([np.broadcast_to(r >> 2, shape), np.broadcast_to(c >> 2, shape),
+                    np.full(shape, bh, dtype=np.int64), np.full(shape, offset, dtype=np.int64)], axis=-1)
+    key = np.array([seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF], dtype=np.uint64)
+    words = philox4x32(ctr.astype(np.uint64), key).astype(np.int64)
+    w = np.take_along_axis(words, np.broadcast_to(r & 3, shape)[..., None], axis=-1)[..., 0]
+    byte = (w >> (8 * np.broadcast_to(c & 3, shape))) & 0xFF
+    return byte >= int(p8)
+
+
+def keep_scale(p8: int) -> float:
+    """1 / (1 - p) for the drop probability p = p8 / 256."""
+    return 256.0 / (256.0 - int(p8))
+
+
+def head_forward(q, k, v, scale, allowed, keep=None, kscale=1.0):
+    """O and LSE for one head: O = P V, or with dropout O = (P o Z) V / (1 - p) (keep bits
+    Z, kscale = 1 / (1 - p)); LSE is that of the softmax before dropout."""
     _, p, lse = head_probabilities(q, k, scale, allowed)
+    if keep is not None:
+        p = p * keep * kscale
     return p @ v, lse
 
 
-def head_backward(q, k, v, do, scale, allowed):
-    """dQ, dK, dV for one head, the gradient of <dO, O>; also returns D = rowsum(P o dP)."""
+def head_backward(q, k, v, do, scale, allowed, keep=None, kscale=1.0):
+    """dQ, dK, dV for one head, the gradient of <dO, O>; also returns D = rowsum(P o dP).
+    With dropout, O = Pd V with Pd = P o Z / (1 - p): dV = Pd^T dO and dP = (dO V^T) o Z / (1 - p),
+    then the same softmax backward."""
     _, p, _ = head_probabilities(q, k, scale, allowed)
-    dv = p.T @ do
+    pd = p if keep is None else p * keep * kscale
+    dv = pd.T @ do
     dp = do @ v.T
+    if keep is not None:
+        dp = dp * keep * kscale
     dsum = (p * dp).sum(axis=1)
     ds = p * (dp - dsum[:, None])
     dq = float(scale) * (ds @ k)
     dk = float(scale) * (ds.T @ q)
     return dq, dk, dv, dsum
+
+
+def _dropout_for(dropout, N, bh):
+    """(keep bits, 1 / (1 - p)) of instance bh for dropout = (p8, seed, offset), or (None, 1)."""
+    if dropout is None or int(dropout[0]) == 0:
+        return None, 1.0
+    p8, seed, offset = (int(x) for x in dropout)
+    return dropout_keep(np.arange(N), np.arange(N), bh, p8, seed, offset), keep_scale(p8)
 
 
 def _f64(x) -> np.ndarray:
@@ -112,11 +158,12 @@ def _heads(B: int, H: int, heads: Optional[Iterable]) -> list:
 
 
 def forward(Q, K, V, scale, causal=False, key_len=None, block_mask=None, block_size=None,
-            heads=None):
+            heads=None, dropout=None):
     """Exact attention forward over [B, H, N, d] inputs.
 
     Returns O [B, H, N, d] and LSE [B, H, N] in float64. With `heads` (a list of
     (b, h)) only those instances are computed; the rest of the outputs are NaN.
+    dropout = (p8, seed, offset) applies dropout_keep's bits to P (None: no dropout).
     """
     B, H, N, d = Q.shape
     O = np.full((B, H, N, d), np.nan)
@@ -124,7 +171,8 @@ def forward(Q, K, V, scale, causal=False, key_len=None, block_mask=None, block_s
     for b, h in _heads(B, H, heads):
         L = None if key_len is None else int(key_len[b])
         ok = allowed_matrix(N, causal, L, block_mask, block_size)
-        O[b, h], LSE[b, h] = head_forward(_f64(Q[b, h]), _f64(K[b, h]), _f64(V[b, h]), scale, ok)
+        keep, ks = _dropout_for(dropout, N, b * H + h)
+        O[b, h], LSE[b, h] = head_forward(_f64(Q[b, h]), _f64(K[b, h]), _f64(V[b, h]), scale, ok, keep, ks)
     return O, LSE
 
 
@@ -230,10 +278,10 @@ def backward_keys(Q, K, V, dO, scale, b, h, keys, causal=False, key_len=None, bl
 
 
 def backward(Q, K, V, dO, scale, causal=False, key_len=None, block_mask=None, block_size=None,
-             heads=None):
+             heads=None, dropout=None):
     """Exact gradients dQ, dK, dV [B, H, N, d] (float64) of <dO, O>.
 
-    With `heads` only those instances are computed; the rest are NaN.
+    With `heads` only those instances are computed; the rest are NaN. `dropout` as in forward().
     """
     B, H, N, d = Q.shape
     dQ = np.full((B, H, N, d), np.nan)
@@ -242,6 +290,7 @@ def backward(Q, K, V, dO, scale, causal=False, key_len=None, block_mask=None, bl
     for b, h in _heads(B, H, heads):
         L = None if key_len is None else int(key_len[b])
         ok = allowed_matrix(N, causal, L, block_mask, block_size)
+        keep, ks = _dropout_for(dropout, N, b * H + h)
         dQ[b, h], dK[b, h], dV[b, h], _ = head_backward(
-            _f64(Q[b, h]), _f64(K[b, h]), _f64(V[b, h]), _f64(dO[b, h]), scale, ok)
+            _f64(Q[b, h]), _f64(K[b, h]), _f64(V[b, h]), _f64(dO[b, h]), scale, ok, keep, ks)
     return dQ, dK, dV

@@ -377,3 +377,88 @@ def test_sampled_rows_and_keys_match_full_oracle(mi):
             dk, dv = oracle.backward_keys(q, k, v, do, sc, b, h, keys, chunk=7, **kw)
             np.testing.assert_allclose(dk, dK[b, h][keys], rtol=0, atol=1e-12)
             np.testing.assert_allclose(dv, dV[b, h][keys], rtol=0, atol=1e-12)
+
+
+# --------------------------------------------------------------------------- dropout
+
+def test_philox_known_answers():
+    """The generator behind the dropout bits reproduces the published known-answer vectors."""
+    import json
+    kat = json.load(open(os.path.join(GOLDEN, "philox4x32_10_kat.json")))
+    for vec in kat["vectors"]:
+        ctr = np.array([int(x, 16) for x in vec["ctr"]], dtype=np.uint64)
+        key = np.array([int(x, 16) for x in vec["key"]], dtype=np.uint64)
+        out = [format(int(x), "08x") for x in oracle.philox4x32(ctr, key)]
+        assert out == vec["out"]
+
+
+def test_dropout_keep_rate_and_indexing():
+    N, p8 = 512, 26
+    keep = oracle.dropout_keep(np.arange(N), np.arange(N), 3, p8, seed=0x1234_5678_9ABC, offset=7)
+    rate = keep.mean()
+    expect = (256 - p8) / 256
+    assert abs(rate - expect) < 5 * np.sqrt(expect * (1 - expect) / keep.size)
+    # any sub-block reads the same bits; other instances / offsets / seeds give other bits
+    rows, cols = np.array([5, 77, 300]), np.array([0, 3, 4, 511])
+    np.testing.assert_array_equal(oracle.dropout_keep(rows, cols, 3, p8, 0x1234_5678_9ABC, 7),
+                                  keep[np.ix_(rows, cols)])
+    for other in [dict(bh=4, seed=0x1234_5678_9ABC, offset=7), dict(bh=3, seed=0x1234_5678_9ABC, offset=8),
+                  dict(bh=3, seed=0x1234_5678_9ABD, offset=7), dict(bh=3, seed=0x1235_5678_9ABC, offset=7)]:
+        k2 = oracle.dropout_keep(np.arange(64), np.arange(64), other["bh"], p8, other["seed"], other["offset"])
+        assert not np.array_equal(k2, keep[:64, :64])
+    assert oracle.dropout_keep(np.arange(8), np.arange(8), 0, 0, 1, 2).all()  # p = 0 keeps everything
+
+
+@pytest.mark.parametrize("mi", range(len(MASKS)))
+def test_dropout_zero_is_plain_attention_and_d_identity(mi):
+    kw = MASKS[mi]
+    rng = np.random.default_rng(90 + mi)
+    B, H, N, d = 2, 2, 12, 8
+    q, k, v, do = (_rand(rng, B, H, N, d) for _ in range(4))
+    O, LSE = oracle.forward(q, k, v, 0.3, **kw)
+    O0, LSE0 = oracle.forward(q, k, v, 0.3, dropout=(0, 5, 6), **kw)
+    np.testing.assert_array_equal(O, O0)
+    np.testing.assert_array_equal(LSE, LSE0)
+    drop = (77, 123456789, 3)
+    Od, LSEd = oracle.forward(q, k, v, 0.3, dropout=drop, **kw)
+    np.testing.assert_array_equal(LSEd, LSE)  # LSE is the softmax's, before dropout
+    for b in range(B):
+        for h in range(H):
+            ok = _allowed_for(N, b, kw)
+            keep = oracle.dropout_keep(np.arange(N), np.arange(N), b * H + h, drop[0], drop[1], drop[2])
+            _, _, _, dsum = oracle.head_backward(q[b, h], k[b, h], v[b, h], do[b, h], 0.3, ok, keep,
+                                                 oracle.keep_scale(drop[0]))
+            # D = rowsum(dO o O) holds with dropout too (the kernels' form of D)
+            np.testing.assert_allclose(dsum, (do[b, h] * Od[b, h]).sum(axis=1), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("mi", range(len(FD_MASKS)))
+def test_dropout_finite_differences(mi):
+    """The dropout backward is the gradient of <dO, O> for fixed keep bits."""
+    kw = dict(FD_MASKS[mi])
+    N, d, drop = 4, 3, (90, 42, 1)
+    if "block_mask" in kw:
+        kw["block_mask"] = np.array([[1, 0], [1, 1]], dtype=np.uint8)
+    rng = np.random.default_rng(95 + mi)
+    q, k, v, do = (_rand(rng, 1, 1, N, d) for _ in range(4))
+    sc = 0.7
+    dQ, dK, dV = oracle.backward(q, k, v, do, sc, dropout=drop, **kw)
+    keep = oracle.dropout_keep(np.arange(N), np.arange(N), 0, drop[0], drop[1], drop[2])
+    assert not keep.all() and keep.any()  # the case does drop some entries
+
+    def loss(q_, k_, v_):
+        o, _ = oracle.forward(q_, k_, v_, sc, dropout=drop, **kw)
+        return float((do * o).sum())
+
+    h = 1e-5
+    for X, G, which in ((q, dQ, 0), (k, dK, 1), (v, dV, 2)):
+        num = np.zeros_like(X)
+        for idx in np.ndindex(X.shape):
+            xp, xm = X.copy(), X.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args_p = [q, k, v]
+            args_m = [q, k, v]
+            args_p[which], args_m[which] = xp, xm
+            num[idx] = (loss(*args_p) - loss(*args_m)) / (2 * h)
+        np.testing.assert_allclose(G, num, rtol=1e-7, atol=1e-9)
