@@ -176,6 +176,8 @@ def main():
     ap.add_argument("--workload", default="C4b")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--dropout", type=float, default=0.0,
+                    help="dropout probability on P (dense workloads; 0: none, the headline step)")
     ap.add_argument("--calibrate-copy", action="store_true", help="only run a 1 GiB device copy (counter scale)")
     ap.add_argument("--digest-counters", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
                                                            "COPY_WRITE_DIR"),
@@ -204,6 +206,7 @@ def main():
 
     case = workloads.make_config(args.workload)
     assert case.dtype == workloads.BF16, "the bench measures bf16 workloads"
+    assert args.dropout == 0.0 or case.block_mask is None, "dropout is for dense workloads"
     dev = torch.device("cuda:0")
     t = {n: torch.from_numpy(case.bits(n).view(np.int16)).view(torch.bfloat16).to(dev)
          for n in ("q", "k", "v", "do")}
@@ -221,9 +224,10 @@ def main():
 
     def step():
         if bmask is None:
-            fa.fwd(t["q"], t["k"], t["v"], scale=sc, causal=case.causal, key_len=key_len, out=o, lse=lse)
+            fa.fwd(t["q"], t["k"], t["v"], scale=sc, causal=case.causal, key_len=key_len, out=o, lse=lse,
+                   dropout_p=args.dropout, seed=1234, offset=0)
             fa.bwd(t["q"], t["k"], t["v"], o, t["do"], lse, scale=sc, causal=case.causal, key_len=key_len,
-                   dq=dq, dk=dk, dv=dv, workspace=ws)
+                   dq=dq, dk=dk, dv=dv, workspace=ws, dropout_p=args.dropout, seed=1234, offset=0)
         else:
             fa.blocksparse_fwd(t["q"], t["k"], t["v"], bmask, case.block_size, scale=sc, causal=case.causal,
                                key_len=key_len, out=o, lse=lse, workspace=ws)
@@ -284,7 +288,7 @@ def main():
                    "H": case.H, "N": case.N, "d": case.d, "seed": case.seed,
                    "mask": "causal" if case.causal else ("block" if bmask is not None else
                                                          ("key_len" if key_len is not None else "none")),
-                   "kept_pairs": pairs, "flop_per_step": flops_step},
+                   "kept_pairs": pairs, "flop_per_step": flops_step, "dropout_p": args.dropout},
         "kernels": {k: {"mean_ms": round(v["mean_ms"], 4), "launches": v["launches"],
                         "share": round(v["share"], 4)} for k, v in kt.items()},
         "roofline": roofline,

@@ -109,8 +109,9 @@ def _workspace(nbytes, ref, workspace):
     return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=ref.device)
 
 
-def fwd(q, k, v, scale=None, causal=False, key_len=None, out=None, lse=None):
-    """Exact attention forward; returns (O, LSE)."""
+def fwd(q, k, v, scale=None, causal=False, key_len=None, out=None, lse=None, dropout_p=0.0, seed=0, offset=0):
+    """Exact attention forward; returns (O, LSE). With dropout_p > 0, dropout on P with keep bits
+    from (seed, offset) (fa_fwd_dropout); the backward must get the same three values."""
     torch = _torch()
     d = _desc(q)
     _same_layout(q, k, v)
@@ -120,6 +121,12 @@ def fwd(q, k, v, scale=None, causal=False, key_len=None, out=None, lse=None):
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
     _lse_check(lse, q)
     kl = _key_len(key_len, q)
+    if dropout_p:
+        st = lib().fa_fwd_dropout(ctypes.byref(d), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                  _scale(scale, q.shape[-1]), int(bool(causal)), _ptr(kl), float(dropout_p),
+                                  int(seed), int(offset), o.data_ptr(), lse.data_ptr(), _stream(q))
+        _check(st, "fa_fwd_dropout")
+        return o, lse
     st = lib().fa_fwd(ctypes.byref(d), q.data_ptr(), k.data_ptr(), v.data_ptr(), _scale(scale, q.shape[-1]),
                       int(bool(causal)), _ptr(kl), o.data_ptr(), lse.data_ptr(), _stream(q))
     _check(st, "fa_fwd")
@@ -127,8 +134,9 @@ def fwd(q, k, v, scale=None, causal=False, key_len=None, out=None, lse=None):
 
 
 def bwd(q, k, v, o, do, lse, scale=None, causal=False, key_len=None, dq=None, dk=None, dv=None,
-        workspace=None):
-    """Exact attention backward; returns (dQ, dK, dV). Use the forward's scale/causal/key_len."""
+        workspace=None, dropout_p=0.0, seed=0, offset=0):
+    """Exact attention backward; returns (dQ, dK, dV). Use the forward's scale, causal, key_len
+    and dropout (dropout_p, seed, offset)."""
     d = _desc(q)
     _same_layout(q, k, v, o, do)
     _lse_check(lse, q)
@@ -139,6 +147,14 @@ def bwd(q, k, v, o, do, lse, scale=None, causal=False, key_len=None, dq=None, dk
     kl = _key_len(key_len, q)
     need = int(lib().fa_bwd_workspace_bytes(ctypes.byref(d)))
     ws = _workspace(need, q, workspace)
+    if dropout_p:
+        st = lib().fa_bwd_dropout(ctypes.byref(d), q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                  do.data_ptr(), lse.data_ptr(), _scale(scale, q.shape[-1]), int(bool(causal)),
+                                  _ptr(kl), float(dropout_p), int(seed), int(offset), dq.data_ptr(),
+                                  dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), ws.numel() * ws.element_size(),
+                                  _stream(q))
+        _check(st, "fa_bwd_dropout")
+        return dq, dk, dv
     st = lib().fa_bwd(ctypes.byref(d), q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
                       lse.data_ptr(), _scale(scale, q.shape[-1]), int(bool(causal)), _ptr(kl), dq.data_ptr(),
                       dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), ws.numel() * ws.element_size(), _stream(q))

@@ -14,8 +14,9 @@ FA_ERR_HIP = -4
 FA_BF16 = 0
 FA_F32 = 1
 
-EXPORTS = ("fa_fwd", "fa_bwd_workspace_bytes", "fa_bwd", "fa_blocksparse_workspace_bytes",
-           "fa_blocksparse_fwd", "fa_blocksparse_bwd", "fa_status_string", "fa_version",
+EXPORTS = ("fa_fwd", "fa_bwd_workspace_bytes", "fa_bwd", "fa_fwd_dropout", "fa_bwd_dropout",
+           "fa_blocksparse_workspace_bytes", "fa_blocksparse_fwd", "fa_blocksparse_bwd", "fa_status_string",
+           "fa_version",
            "fa_timer_enable", "fa_timer_reset", "fa_timer_read")
 
 
@@ -58,6 +59,10 @@ def _load():
         "fa_fwd": (ctypes.c_int, [DESC, P, P, P, F32, ctypes.c_int, P, P, P, P]),
         "fa_bwd_workspace_bytes": (SZ, [DESC]),
         "fa_bwd": (ctypes.c_int, [DESC, P, P, P, P, P, P, F32, ctypes.c_int, P, P, P, P, P, SZ, P]),
+        "fa_fwd_dropout": (ctypes.c_int, [DESC, P, P, P, F32, ctypes.c_int, P, F32, ctypes.c_uint64,
+                                          ctypes.c_uint32, P, P, P]),
+        "fa_bwd_dropout": (ctypes.c_int, [DESC, P, P, P, P, P, P, F32, ctypes.c_int, P, F32, ctypes.c_uint64,
+                                          ctypes.c_uint32, P, P, P, P, SZ, P]),
         "fa_blocksparse_workspace_bytes": (SZ, [DESC, I32, ctypes.c_int]),
         "fa_blocksparse_fwd": (ctypes.c_int, [DESC, P, P, P, F32, ctypes.c_int, P, P, I32, P, P, P, SZ, P]),
         "fa_blocksparse_bwd": (ctypes.c_int, [DESC, P, P, P, P, P, P, F32, ctypes.c_int, P, P, I32, P, P, P,

@@ -267,6 +267,49 @@ extern "C" int fa_bwd(const fa_desc* desc, const void* Q, const void* K, const v
   return hip_status(launch_bwd_bf16(a, static_cast<hipStream_t>(stream)));
 }
 
+// Dropout parameters: p in [0, 1), quantised to p8 = round(256 p) <= 255.
+int make_dropout(float p, uint64_t seed, uint32_t offset, Dropout& d) {
+  if (!(p >= 0.f) || !(p < 1.f)) return FA_ERR_INVALID;  // (also rejects NaN)
+  const int p8 = (int)lrintf(p * 256.f);
+  if (p8 > 255) return FA_ERR_INVALID;
+  d.p8 = (uint32_t)p8;
+  d.k0 = (uint32_t)(seed & 0xFFFFFFFFu);
+  d.k1 = (uint32_t)(seed >> 32);
+  d.offset = offset;
+  d.scale = 256.f / (float)(256 - p8);
+  return FA_OK;
+}
+
+extern "C" int fa_fwd_dropout(const fa_desc* desc, const void* Q, const void* K, const void* V, float scale,
+                              int causal, const int32_t* key_len, float dropout_p, uint64_t seed,
+                              uint32_t offset, void* O, float* LSE, void* stream) {
+  int st = check_desc(desc);
+  if (st) return st;
+  if ((st = check_scale(scale))) return st;
+  if ((st = check_ptrs({Q, K, V, O, LSE}))) return st;
+  FwdArgs a = fwd_args(desc, Q, K, V, scale, causal, key_len, O, LSE);
+  if ((st = make_dropout(dropout_p, seed, offset, a.dropout))) return st;
+  if (a.dropout.p8 && desc->dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return hip_status(desc->dtype == FA_BF16 ? launch_fwd_bf16(a, s) : launch_fwd_f32(a, s));
+}
+
+extern "C" int fa_bwd_dropout(const fa_desc* desc, const void* Q, const void* K, const void* V, const void* O,
+                              const void* dO, const float* LSE, float scale, int causal, const int32_t* key_len,
+                              float dropout_p, uint64_t seed, uint32_t offset, void* dQ, void* dK, void* dV,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_desc(desc);
+  if (st) return st;
+  if (desc->dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if ((st = check_scale(scale))) return st;
+  if ((st = check_ptrs({Q, K, V, O, dO, LSE, dQ, dK, dV}))) return st;
+  if (!workspace || !aligned16(workspace) || workspace_bytes < bwd_ws_bytes(desc)) return FA_ERR_WORKSPACE;
+  BwdArgs a = bwd_args(desc, Q, K, V, O, dO, LSE, scale, causal, key_len, dQ, dK, dV);
+  if ((st = make_dropout(dropout_p, seed, offset, a.dropout))) return st;
+  carve_bwd(desc, workspace, a);
+  return hip_status(launch_bwd_bf16(a, static_cast<hipStream_t>(stream)));
+}
+
 extern "C" size_t fa_blocksparse_workspace_bytes(const fa_desc* desc, int32_t block_size, int backward) {
   if (check_desc(desc) || check_block(desc, block_size)) return 0;
   const size_t lists = lists_bytes(desc->N / block_size);

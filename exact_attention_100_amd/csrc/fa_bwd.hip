@@ -48,6 +48,7 @@ struct BwdKParams {
   const int32_t* row_idx;
   int bs;
   int n_blocks;            // 128-row blocks of N
+  Dropout drop;            // p8 == 0: none
 };
 
 constexpr int kBwdBlock = 128;  // keys (dK/dV pass) or queries (dQ pass) per workgroup
@@ -108,7 +109,10 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdKParams p) {
 // VGPRs, which keeps the d = 128 kernel within 256 registers (two waves per SIMD).
 // SMASK: a block-sparse launch that also applies the causal / key-length
 // element masks (without it, sparse tiles are never masked).
-template <int D, int BRQ, bool SPARSE, bool VLDS, bool SMASK = false>
+// DROP: dropout on P (dense launches), the keep bits regenerated from the same
+// counters as the forward: dV takes P o Z / (1 - p) and dP is masked and scaled
+// the same way before dS = P (dP - D).
+template <int D, int BRQ, bool SPARSE, bool VLDS, bool SMASK = false, bool DROP = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FA_BWD_WAVES_PER_EU)))
 void bwd_dkdv_kernel(BwdKParams p) {
   constexpr int NQB = BRQ / 32;
@@ -267,12 +271,27 @@ void bwd_dkdv_kernel(BwdKParams p) {
         for (int j = 0; j < 4; ++j) {
           const f32x4 lv = *reinterpret_cast<const f32x4*>(&lr[32 * sb + 8 * j + 4 * g]);
           const f32x4 dv = *reinterpret_cast<const f32x4*>(&dlr[32 * sb + 8 * j + 4 * g]);
+          // Dropout: registers 4 j .. 4 j + 3 are queries qb4 .. qb4 + 3 of this lane's
+          // key, i.e. byte (key mod 4) of words 0..3 of one counter.
+          u32x4 w = {};
+          if (DROP) {
+            const int qb4 = q0 + 32 * sb + 8 * j + 4 * g;
+            w = philox4x32_10((uint32_t)qb4 >> 2, (uint32_t)mykey >> 2, (uint32_t)inst, p.drop.offset, p.drop.k0,
+                              p.drop.k1);
+          }
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int r = 4 * j + i;
             const float pr = fast_exp2(fmaf(sacc[sb][r], p.c, -lv[i]));
-            sacc[sb][r] = pr;
-            dpacc[sb][r] = pr * (dpacc[sb][r] - dv[i]);
+            if (DROP) {
+              const bool keep = ((w[i] >> (8 * (mykey & 3))) & 0xFFu) >= p.drop.p8;
+              const float z = keep ? p.drop.scale : 0.f;
+              sacc[sb][r] = pr * z;                              // dropped P, for dV
+              dpacc[sb][r] = pr * (dpacc[sb][r] * z - dv[i]);    // dS = P (dP o Z / (1 - p) - D)
+            } else {
+              sacc[sb][r] = pr;
+              dpacc[sb][r] = pr * (dpacc[sb][r] - dv[i]);
+            }
           }
         }
 
@@ -347,7 +366,7 @@ void bwd_dkdv_kernel(BwdKParams p) {
 //                                   B = dS^T straight from the accumulator layout).
 // Loads past the end are clamped to the last row: such keys are masked (P = 0)
 // and such queries are not stored.
-template <int D, int BC, bool SPARSE, bool SMASK = false>
+template <int D, int BC, bool SPARSE, bool SMASK = false, bool DROP = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FA_BWD_WAVES_PER_EU)))
 void bwd_dq_kernel(BwdKParams p) {
   constexpr int NKB = BC / 32;
@@ -470,9 +489,21 @@ void bwd_dq_kernel(BwdKParams p) {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float pr = fast_exp2(fmaf(sacc[kb][r], p.c, -lse2_q));
-        dpacc[kb][r] = pr * (dpacc[kb][r] - d_q);
+      for (int q4 = 0; q4 < 4; ++q4) {
+        // Dropout: registers 4 q4 .. 4 q4 + 3 are one key quad of this lane's query.
+        uint32_t w = 0;
+        if (DROP) w = dropout_row_word(p.drop, qrow, kv0 + 32 * kb + 8 * q4 + 4 * g, (uint32_t)inst);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int r = 4 * q4 + c;
+          const float pr = fast_exp2(fmaf(sacc[kb][r], p.c, -lse2_q));
+          if (DROP) {
+            const float z = ((w >> (8 * c)) & 0xFFu) >= p.drop.p8 ? p.drop.scale : 0.f;
+            dpacc[kb][r] = pr * (dpacc[kb][r] * z - d_q);
+          } else {
+            dpacc[kb][r] = pr * (dpacc[kb][r] - d_q);
+          }
+        }
       }
     bf16x8 dsb[2 * NKB];
 #pragma unroll
@@ -550,6 +581,8 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s) {
   p.n_blocks = (a.N + kBwdBlock - 1) / kBwdBlock;
   const bool sparse = a.col_ptr != nullptr;
   const bool smask = a.causal || a.key_len != nullptr;
+  const bool drop = a.dropout.p8 != 0 && !sparse;
+  p.drop = a.dropout;
   const int64_t rows = (int64_t)a.B * a.H * a.N;
   const dim3 block(256);
 
@@ -567,11 +600,13 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)(a.B * a.H * p.n_blocks));
   timer_begin("fa_bwd_dkdv", s);
   if (a.d == 128) {
-    if (sparse && smask) bwd_dkdv_kernel<128, TQ128, true, true, true><<<grid, block, 0, s>>>(p);
+    if (drop) bwd_dkdv_kernel<128, TQ128, false, true, false, true><<<grid, block, 0, s>>>(p);
+    else if (sparse && smask) bwd_dkdv_kernel<128, TQ128, true, true, true><<<grid, block, 0, s>>>(p);
     else if (sparse) bwd_dkdv_kernel<128, TQ128, true, true><<<grid, block, 0, s>>>(p);
     else bwd_dkdv_kernel<128, TQ128, false, true><<<grid, block, 0, s>>>(p);
   } else {
-    if (sparse && smask) bwd_dkdv_kernel<64, TQ64, true, false, true><<<grid, block, 0, s>>>(p);
+    if (drop) bwd_dkdv_kernel<64, TQ64, false, false, false, true><<<grid, block, 0, s>>>(p);
+    else if (sparse && smask) bwd_dkdv_kernel<64, TQ64, true, false, true><<<grid, block, 0, s>>>(p);
     else if (sparse) bwd_dkdv_kernel<64, TQ64, true, false><<<grid, block, 0, s>>>(p);
     else bwd_dkdv_kernel<64, TQ64, false, false><<<grid, block, 0, s>>>(p);
   }
@@ -581,11 +616,13 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s) {
 
   timer_begin("fa_bwd_dq", s);
   if (a.d == 128) {
-    if (sparse && smask) bwd_dq_kernel<128, TK128, true, true><<<grid, block, 0, s>>>(p);
+    if (drop) bwd_dq_kernel<128, TK128, false, false, true><<<grid, block, 0, s>>>(p);
+    else if (sparse && smask) bwd_dq_kernel<128, TK128, true, true><<<grid, block, 0, s>>>(p);
     else if (sparse) bwd_dq_kernel<128, TK128, true><<<grid, block, 0, s>>>(p);
     else bwd_dq_kernel<128, TK128, false><<<grid, block, 0, s>>>(p);
   } else {
-    if (sparse && smask) bwd_dq_kernel<64, TK64, true, true><<<grid, block, 0, s>>>(p);
+    if (drop) bwd_dq_kernel<64, TK64, false, false, true><<<grid, block, 0, s>>>(p);
+    else if (sparse && smask) bwd_dq_kernel<64, TK64, true, true><<<grid, block, 0, s>>>(p);
     else if (sparse) bwd_dq_kernel<64, TK64, true><<<grid, block, 0, s>>>(p);
     else bwd_dq_kernel<64, TK64, false><<<grid, block, 0, s>>>(p);
   }

@@ -302,6 +302,66 @@ struct TileOffsets {
   }
 };
 
+// Dropout keep bits from Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel
+// Random Numbers: As Easy as 1, 2, 3", SC 2011): 4 x 32-bit counter, 2 x 32-bit
+// key, ten rounds of two 32 x 32 -> 64-bit products mixed by XOR, the key bumped
+// by the Weyl constants between rounds. The pair (query i, key j) of instance
+// bh takes byte (j mod 4) of word (i mod 4) at counter (i div 4, j div 4, bh,
+// offset) and is kept iff that byte is >= p8 (drop probability p8 / 256), so
+// one call serves a 4 x 4 block of pairs.
+struct Dropout {
+  uint32_t p8;       // 1..255 (0: the kernels are built without dropout)
+  uint32_t k0, k1;   // seed, low and high words
+  uint32_t offset;   // counter word 3
+  float scale;       // 1 / (1 - p8 / 256)
+};
+__device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                               uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c0, p1 = (uint64_t)0xCD9E8D57u * c2;
+    const uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
+    const uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
+    c0 = hi1 ^ c1 ^ k0;
+    c1 = lo1;
+    c2 = hi0 ^ c3 ^ k1;
+    c3 = lo0;
+  }
+  u32x4 r;
+  r[0] = c0;
+  r[1] = c1;
+  r[2] = c2;
+  r[3] = c3;
+  return r;
+}
+// The four keep bytes of query i for keys 4 (j div 4) .. + 3 (byte c <-> key + c).
+__device__ __forceinline__ uint32_t dropout_row_word(const Dropout& d, int i, int j, uint32_t bh) {
+  const u32x4 w = philox4x32_10((uint32_t)i >> 2, (uint32_t)j >> 2, bh, d.offset, d.k0, d.k1);
+  const int r = i & 3;
+  return r == 0 ? w[0] : (r == 1 ? w[1] : (r == 2 ? w[2] : w[3]));
+}
+// 0xFFFF in each 16-bit half of a packed bf16 pair whose pair is kept: bytes c
+// and c + 1 of `w` against p8.
+__device__ __forceinline__ uint32_t dropout_pair_mask(uint32_t w, int c, uint32_t p8) {
+  const uint32_t lo = ((w >> (8 * c)) & 0xFFu) >= p8 ? 0x0000FFFFu : 0u;
+  const uint32_t hi = ((w >> (8 * c + 8)) & 0xFFu) >= p8 ? 0xFFFF0000u : 0u;
+  return lo | hi;
+}
+// Zeroes the dropped entries of an 8-value packed operand holding two key quads
+// (words w_a for values 0..3, w_b for values 4..7).
+__device__ __forceinline__ bf16x8 dropout_apply8(bf16x8 v, uint32_t w_a, uint32_t w_b, uint32_t p8) {
+  u32x4 u = __builtin_bit_cast(u32x4, v);
+  u[0] &= dropout_pair_mask(w_a, 0, p8);
+  u[1] &= dropout_pair_mask(w_a, 2, p8);
+  u[2] &= dropout_pair_mask(w_b, 0, p8);
+  u[3] &= dropout_pair_mask(w_b, 2, p8);
+  return __builtin_bit_cast(bf16x8, u);
+}
+
 // Compile-time flag for generic lambdas (selects the masked / unmasked variant
 // of a tile body without per-element branches).
 template <bool B>

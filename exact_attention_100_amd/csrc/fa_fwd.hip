@@ -41,6 +41,7 @@ struct FwdKParams {
   const int32_t* col_idx;
   int bs;
   int n_qblocks;
+  Dropout drop;
 };
 
 constexpr int kFwdRows = 128;  // query rows per workgroup (4 waves x 32)
@@ -191,8 +192,10 @@ __device__ __forceinline__ float softmax_tile_bf16(f32x16 (&s)[NKB], float c, fl
 #endif
 
 // SMASK: a block-sparse launch that also applies the causal / key-length
-// element masks (without it, sparse tiles are never masked).
-template <int D, int BC, bool SPARSE, bool SMASK = false>
+// element masks (without it, sparse tiles are never masked). DROP: dropout on P
+// (dense launches): dropped entries of the packed bf16 probabilities are zeroed
+// after their row sum is taken, and O is scaled by 1 / (1 - p) at the end.
+template <int D, int BC, bool SPARSE, bool SMASK = false, bool DROP = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FA_FWD_WAVES_PER_EU)))
 void fwd_bf16_kernel(FwdKParams p) {
   constexpr int NKB = BC / 32;
@@ -289,6 +292,19 @@ void fwd_bf16_kernel(FwdKParams p) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db) oacc[db] = mfma_bf16(to.read_tr(sv, ks, db), pb[ks], oacc[db]);
   };
+  // Dropout of one tile's packed probabilities (k-step ks = 2 kb + s holds the key
+  // quads 32 kb + 16 s + 4 g and that + 8 of this lane's query).
+  auto drop_tile = [&](bf16x8 (&pk)[2 * NKB], int kv0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int key_a = kv0 + 32 * kb + 16 * s + 4 * g;
+        const uint32_t wa = dropout_row_word(p.drop, qrow, key_a, (uint32_t)inst);
+        const uint32_t wb = dropout_row_word(p.drop, qrow, key_a + 8, (uint32_t)inst);
+        pk[2 * kb + s] = dropout_apply8(pk[2 * kb + s], wa, wb, p.drop.p8);
+      }
+  };
   auto needs_mask = [&](int kv0) {
     return (!SPARSE || SMASK) && ((kv0 + BC > rg.kv_len) || (p.causal && kv0 + BC - 1 > q0 + wave * 32));
   };
@@ -307,6 +323,7 @@ void fwd_bf16_kernel(FwdKParams p) {
       // P^T as B operands: k-step ks = 2 kb + s covers keys 32 kb + 16 s +
       // {4g..4g+3, 8+4g..8+4g+3}. (alpha is irrelevant: nothing accumulated yet.)
       softmax_tile_bf16<NKB>(sacc, p.c, m_run, l_run, pb);
+      if (DROP) drop_tile(pb, kv0_of(0));
     }
     wait_vmem();
     __syncthreads();
@@ -376,6 +393,7 @@ void fwd_bf16_kernel(FwdKParams p) {
 #pragma unroll
       for (int i = 0; i < 2 * NKB; ++i) asm volatile("" : "+v"(pbn[i]));
       asm volatile("" : "+v"(rs), "+v"(alpha), "+v"(m_new));
+      if (DROP) drop_tile(pbn, kv0);
       const float m_prev = m_run;
       m_run = m_new;
       l_run = l_run * alpha + rs;
@@ -400,7 +418,7 @@ void fwd_bf16_kernel(FwdKParams p) {
 
   // Epilogue: O = O_acc / l, LSE = (m + log2 l) ln 2. Rows with no key: O = 0, LSE = -inf.
   const float l_tot = pair_sum(l_run);
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  const float inv = l_tot > 0.f ? (DROP ? p.drop.scale : 1.f) / l_tot : 0.f;
   if (qrow < N) {
     bf16* Orow = static_cast<bf16*>(p.o) + base + (int64_t)qrow * p.sn;
 #pragma unroll
@@ -560,6 +578,7 @@ static FwdKParams make_params(const FwdArgs& a) {
   p.col_idx = a.col_idx;
   p.bs = a.block_size;
   p.n_qblocks = (a.N + kFwdRows - 1) / kFwdRows;
+  p.drop = a.dropout;
   return p;
 }
 
@@ -582,7 +601,10 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s) {
   const bool smask = a.causal || a.key_len != nullptr;
   timer_begin("fa_fwd_bf16", s);
   constexpr int BC128 = FA_FWD_BC_D128, BC64 = FA_FWD_BC_D64, BCS64 = FA_FWD_BC_SPARSE_D64;
-  if (a.d == 128) {
+  if (a.dropout.p8 && !sparse) {
+    if (a.d == 128) fwd_bf16_kernel<128, BC128, false, false, true><<<grid, block, 0, s>>>(p);
+    else fwd_bf16_kernel<64, BC64, false, false, true><<<grid, block, 0, s>>>(p);
+  } else if (a.d == 128) {
     if (sparse && smask) fwd_bf16_kernel<128, BC128, true, true><<<grid, block, 0, s>>>(p);
     else if (sparse) fwd_bf16_kernel<128, BC128, true><<<grid, block, 0, s>>>(p);
     else fwd_bf16_kernel<128, BC128, false><<<grid, block, 0, s>>>(p);

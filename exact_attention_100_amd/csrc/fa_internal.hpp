@@ -2,6 +2,8 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#include "fa_common.hpp"
 #include <stdint.h>
 
 namespace fa {
@@ -22,6 +24,7 @@ struct FwdArgs {
   const int32_t* row_ptr;
   const int32_t* col_idx;
   int block_size;
+  Dropout dropout;  // p8 == 0: none
 };
 
 struct BwdArgs {
@@ -49,6 +52,7 @@ struct BwdArgs {
   const int32_t* col_ptr;
   const int32_t* row_idx;
   int block_size;
+  Dropout dropout;  // p8 == 0: none
 };
 
 // Kernel timer hooks (fa_api.hip): bracket one launch with events.

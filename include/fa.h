@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define FA_VERSION 101
+#define FA_VERSION 102
 
 enum fa_status {
   FA_OK = 0,
@@ -124,6 +124,28 @@ int fa_blocksparse_bwd(const fa_desc* desc, const void* Q, const void* K, const 
                        const int32_t* key_len, const uint8_t* block_mask, int32_t block_size,
                        void* dQ, void* dK, void* dV, void* workspace, size_t workspace_bytes,
                        void* stream);
+
+/* Forward with dropout on P (reading notes, §Algorithm › Tiling and Kernel
+ * Fusion: the fused kernel applies dropout after the softmax): as fa_fwd, but
+ * O = (P o Z) V / (1 - p) with keep bits Z drawn per (instance, query, key) from
+ * Philox4x32-10 (Salmon et al., SC 2011): pair (i, j) of instance bh = b H + h
+ * takes byte j mod 4 of word i mod 4 at counter (i div 4, j div 4, bh, offset)
+ * with key (seed low word, seed high word), and is kept iff that byte is >=
+ * p8 = round(256 dropout_p); the drop probability applied is p8 / 256. LSE is
+ * that of the softmax before dropout. dropout_p must lie in [0, 1) (else
+ * FA_ERR_INVALID); p8 = 0 is fa_fwd. bf16 only when p8 > 0 (else
+ * FA_ERR_UNSUPPORTED). Dense, causal and key_len masks; not block-sparse. */
+int fa_fwd_dropout(const fa_desc* desc, const void* Q, const void* K, const void* V, float scale,
+                   int causal, const int32_t* key_len, float dropout_p, uint64_t seed,
+                   uint32_t offset, void* O, float* LSE, void* stream);
+
+/* Backward of fa_fwd_dropout: the keep bits are regenerated from the same
+ * (seed, offset), which must match the forward's, as must scale, causal and
+ * key_len. Same workspace as fa_bwd. */
+int fa_bwd_dropout(const fa_desc* desc, const void* Q, const void* K, const void* V, const void* O,
+                   const void* dO, const float* LSE, float scale, int causal, const int32_t* key_len,
+                   float dropout_p, uint64_t seed, uint32_t offset, void* dQ, void* dK, void* dV,
+                   void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static, human-readable name of a status code. */
 const char* fa_status_string(int status);
