@@ -227,6 +227,20 @@ void bwd_dkdv_kernel(BwdKParams p) {
       // its own tile); every wave finished reading them before the previous barrier.
       issue_tile(tile_q0(min(t + 1, n_qt - 1)), qw, dow, lw, dlw);
 
+      // Dropout keep bits of this tile, bit 16 sb + r for register r of query block sb,
+      // computed before the products while few registers are live: registers
+      // 4 j .. 4 j + 3 are queries qb4 .. qb4 + 3 of this lane's key, i.e. byte
+      // (key mod 4) of words 0..3 at one counter.
+      // Dropout keep bits of this tile, bit 16 sb + r for register r of query block sb
+      // (registers 4 j .. 4 j + 3 are query quad q0 + 4 g + 8 (4 sb + j)), computed
+      // before the products while few registers are live.
+      uint32_t keepbits = 0;
+      if (DROP) {
+        keepbits = dropout_col_bits<4 * NQB>(p.drop, mykey, q0 + 4 * g, (uint32_t)inst);
+        asm volatile("" : "+v"(keepbits));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+
       // S = Q_i K_w^T and dP = dO_i V_w^T (rows = queries, columns = this wave's keys).
       f32x16 sacc[NQB], dpacc[NQB];
 #pragma unroll
@@ -271,24 +285,19 @@ void bwd_dkdv_kernel(BwdKParams p) {
         for (int j = 0; j < 4; ++j) {
           const f32x4 lv = *reinterpret_cast<const f32x4*>(&lr[32 * sb + 8 * j + 4 * g]);
           const f32x4 dv = *reinterpret_cast<const f32x4*>(&dlr[32 * sb + 8 * j + 4 * g]);
-          // Dropout: registers 4 j .. 4 j + 3 are queries qb4 .. qb4 + 3 of this lane's
-          // key, i.e. byte (key mod 4) of words 0..3 of one counter.
-          u32x4 w = {};
-          if (DROP) {
-            const int qb4 = q0 + 32 * sb + 8 * j + 4 * g;
-            w = philox4x32_10((uint32_t)qb4 >> 2, (uint32_t)mykey >> 2, (uint32_t)inst, p.drop.offset, p.drop.k0,
-                              p.drop.k1);
-          }
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int r = 4 * j + i;
-            const float pr = fast_exp2(fmaf(sacc[sb][r], p.c, -lv[i]));
             if (DROP) {
-              const bool keep = ((w[i] >> (8 * (mykey & 3))) & 0xFFu) >= p.drop.p8;
-              const float z = keep ? p.drop.scale : 0.f;
-              sacc[sb][r] = pr * z;                              // dropped P, for dV
-              dpacc[sb][r] = pr * (dpacc[sb][r] * z - dv[i]);    // dS = P (dP o Z / (1 - p) - D)
+              // In place (a second set of temporaries would not fit in the registers):
+              // dS = P (dP o Z / (1 - p) - D), then the dropped P o Z / (1 - p) for dV.
+              const float z = ((keepbits >> (16 * sb + r)) & 1u) ? p.drop.scale : 0.f;
+              dpacc[sb][r] = fmaf(dpacc[sb][r], z, -dv[i]);
+              sacc[sb][r] = fast_exp2(fmaf(sacc[sb][r], p.c, -lv[i]));
+              dpacc[sb][r] *= sacc[sb][r];
+              sacc[sb][r] *= z;
             } else {
+              const float pr = fast_exp2(fmaf(sacc[sb][r], p.c, -lv[i]));
               sacc[sb][r] = pr;
               dpacc[sb][r] = pr * (dpacc[sb][r] - dv[i]);
             }
@@ -486,13 +495,15 @@ void bwd_dq_kernel(BwdKParams p) {
           if (!ok) sacc[kb][r] = kNegInf;
         }
     }
+    // Dropout: registers 4 q4 .. 4 q4 + 3 of block kb are key quad c = 4 kb + q4
+    // (keys kv0 + 4 g + 8 c .. + 3) of this lane's query.
+    uint32_t dw[4 * NKB];
+    if (DROP) dropout_row_words<4 * NKB>(p.drop, qrow, kv0 + 4 * g, (uint32_t)inst, dw);
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        // Dropout: registers 4 q4 .. 4 q4 + 3 are one key quad of this lane's query.
-        uint32_t w = 0;
-        if (DROP) w = dropout_row_word(p.drop, qrow, kv0 + 32 * kb + 8 * q4 + 4 * g, (uint32_t)inst);
+        const uint32_t w = DROP ? dw[4 * kb + q4] : 0u;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           const int r = 4 * q4 + c;

@@ -338,12 +338,69 @@ __device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
   r[3] = c3;
   return r;
 }
-// The four keep bytes of query i for keys 4 (j div 4) .. + 3 (byte c <-> key + c).
-__device__ __forceinline__ uint32_t dropout_row_word(const Dropout& d, int i, int j, uint32_t bh) {
-  const u32x4 w = philox4x32_10((uint32_t)i >> 2, (uint32_t)j >> 2, bh, d.offset, d.k0, d.k1);
-  const int r = i & 3;
-  return r == 0 ? w[0] : (r == 1 ? w[1] : (r == 2 ? w[2] : w[3]));
+// Lane r of each group of four lanes receives v from lane r ^ k (k = 1, 2, 3; DPP).
+__device__ __forceinline__ uint32_t quad_xor(uint32_t v, int k) {
+  return k == 1 ? (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false)    // [1,0,3,2]
+                : (k == 2 ? (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false)   // [2,3,0,1]
+                          : (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x1B, 0xF, 0xF, false));  // [3,2,1,0]
 }
+
+// Keep words of NC key quads (keys key0 + 8 c .. + 3) for this lane's query i,
+// where the four lanes of each lane quad hold queries 4 m .. 4 m + 3 (i mod 4 =
+// lane mod 4). The four lanes need the same generator calls (one word each), so
+// each lane computes one call in four and the words are exchanged within the
+// quad. All 64 lanes must be active.
+template <int NC>
+__device__ __forceinline__ void dropout_row_words(const Dropout& d, int i, int key0, uint32_t bh,
+                                                  uint32_t (&out)[NC]) {
+  static_assert(NC % 4 == 0, "key quads come in groups of four");
+  const int t = i & 3;
+#pragma unroll
+  for (int c0 = 0; c0 < NC; c0 += 4) {
+    const u32x4 w = philox4x32_10((uint32_t)i >> 2, (uint32_t)(key0 + 8 * (c0 + t)) >> 2, bh, d.offset, d.k0, d.k1);
+    uint32_t got[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int want = t ^ k;  // the word the partner lane (t ^ k) needs
+      const uint32_t send = want == 0 ? w[0] : (want == 1 ? w[1] : (want == 2 ? w[2] : w[3]));
+      got[k] = k == 0 ? send : quad_xor(send, k);  // my word of quad c0 + (t ^ k)
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int k = j ^ t;
+      out[c0 + j] = k == 0 ? got[0] : (k == 1 ? got[1] : (k == 2 ? got[2] : got[3]));
+    }
+  }
+}
+
+// Keep bits of this lane's key j for NC query quads (queries q4 + 8 c .. + 3):
+// bit 4 c + w is query q4 + 8 c + w. The four lanes of each lane quad hold keys
+// 4 m .. 4 m + 3 (j mod 4 = lane mod 4) and need the same calls (one byte of
+// each word), so each lane computes one call in four, reduces it to its 4 x 4
+// keep bits and hands each partner its column. All 64 lanes must be active.
+template <int NC>
+__device__ __forceinline__ uint32_t dropout_col_bits(const Dropout& d, int j, int q4, uint32_t bh) {
+  static_assert(NC % 4 == 0 && NC <= 8, "query quads come in groups of four, 32 bits at most");
+  const int t = j & 3;
+  uint32_t bits = 0;
+#pragma unroll
+  for (int c0 = 0; c0 < NC; c0 += 4) {
+    const u32x4 w = philox4x32_10((uint32_t)(q4 + 8 * (c0 + t)) >> 2, (uint32_t)j >> 2, bh, d.offset, d.k0, d.k1);
+    uint32_t kb = 0;  // bit 4 b + r: key byte b of query row r kept
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) kb |= (((w[r] >> (8 * b)) & 0xFFu) >= d.p8 ? 1u : 0u) << (4 * b + r);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t send = (kb >> (4 * (t ^ k))) & 0xFu;  // the partner's key column
+      const uint32_t got = k == 0 ? send : quad_xor(send, k);
+      bits |= got << (4 * (c0 + (t ^ k)));
+    }
+  }
+  return bits;
+}
+
 // 0xFFFF in each 16-bit half of a packed bf16 pair whose pair is kept: bytes c
 // and c + 1 of `w` against p8.
 __device__ __forceinline__ uint32_t dropout_pair_mask(uint32_t w, int c, uint32_t p8) {

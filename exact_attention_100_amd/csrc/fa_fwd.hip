@@ -294,16 +294,15 @@ void fwd_bf16_kernel(FwdKParams p) {
   };
   // Dropout of one tile's packed probabilities (k-step ks = 2 kb + s holds the key
   // quads 32 kb + 16 s + 4 g and that + 8 of this lane's query).
+  // (Quad c = 4 kb + 2 s + h is keys kv0 + 4 g + 8 c .. + 3.)
   auto drop_tile = [&](bf16x8 (&pk)[2 * NKB], int kv0) __attribute__((always_inline)) {
+    uint32_t w[4 * NKB];
+    dropout_row_words<4 * NKB>(p.drop, qrow, kv0 + 4 * g, (uint32_t)inst, w);
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const int key_a = kv0 + 32 * kb + 16 * s + 4 * g;
-        const uint32_t wa = dropout_row_word(p.drop, qrow, key_a, (uint32_t)inst);
-        const uint32_t wb = dropout_row_word(p.drop, qrow, key_a + 8, (uint32_t)inst);
-        pk[2 * kb + s] = dropout_apply8(pk[2 * kb + s], wa, wb, p.drop.p8);
-      }
+      for (int s = 0; s < 2; ++s)
+        pk[2 * kb + s] = dropout_apply8(pk[2 * kb + s], w[4 * kb + 2 * s], w[4 * kb + 2 * s + 1], p.drop.p8);
   };
   auto needs_mask = [&](int kv0) {
     return (!SPARSE || SMASK) && ((kv0 + BC > rg.kv_len) || (p.causal && kv0 + BC - 1 > q0 + wave * 32));
