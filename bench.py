@@ -176,6 +176,8 @@ def main():
     ap.add_argument("--workload", default="C4b")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--lib", default=None,
+                    help="load this build of the library instead of the package's (tile-size variants)")
     ap.add_argument("--dropout", type=float, default=0.0,
                     help="dropout probability on P (dense workloads; 0: none, the headline step)")
     ap.add_argument("--calibrate-copy", action="store_true", help="only run a 1 GiB device copy (counter scale)")
@@ -200,7 +202,11 @@ def main():
     import exact_attention_100_amd as fa
     import workloads
     from exact_attention_100_amd import _lib
-    if not os.path.exists(_lib.LIB_PATH):
+    if args.lib:
+        _lib.LIB_PATH = os.path.abspath(args.lib)
+        if not os.path.exists(_lib.LIB_PATH):
+            sys.exit(f"{args.lib} is not built (python -m exact_attention_100_amd.build --out {args.lib} -D ...)")
+    elif not os.path.exists(_lib.LIB_PATH):
         from exact_attention_100_amd.build import build
         build()
 
@@ -288,7 +294,8 @@ def main():
                    "H": case.H, "N": case.N, "d": case.d, "seed": case.seed,
                    "mask": "causal" if case.causal else ("block" if bmask is not None else
                                                          ("key_len" if key_len is not None else "none")),
-                   "kept_pairs": pairs, "flop_per_step": flops_step, "dropout_p": args.dropout},
+                   "kept_pairs": pairs, "flop_per_step": flops_step, "dropout_p": args.dropout,
+                   "library": os.path.relpath(_lib.LIB_PATH, ROOT)},
         "kernels": {k: {"mean_ms": round(v["mean_ms"], 4), "launches": v["launches"],
                         "share": round(v["share"], 4)} for k, v in kt.items()},
         "roofline": roofline,

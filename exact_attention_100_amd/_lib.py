@@ -4,7 +4,10 @@ from __future__ import annotations
 import ctypes
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libfa.so")
+# The in-tree build; EXACT_ATTENTION_LIB selects another build of the same sources (tile-size
+# variants made by build.py --out, for measurements and their parity checks).
+LIB_PATH = os.environ.get("EXACT_ATTENTION_LIB") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "lib", "libfa.so")
 
 FA_OK = 0
 FA_ERR_INVALID = -1

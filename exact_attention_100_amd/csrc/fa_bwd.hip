@@ -359,9 +359,10 @@ void bwd_dkdv_kernel(BwdKParams p) {
 
 // ------------------------------------------------------------------------------ dQ
 
-// Keys per tile of the dQ pass, per head dim (32 keeps d = 128 within 256 registers).
+// Keys per tile of the dQ pass, per head dim (64 at d = 128 just fits 256 registers and
+// measured 6% faster than 32 at N = 8192).
 #ifndef FA_BWD_TILE_K_D128
-#define FA_BWD_TILE_K_D128 32
+#define FA_BWD_TILE_K_D128 64
 #endif
 #ifndef FA_BWD_TILE_K_D64
 #define FA_BWD_TILE_K_D64 64
@@ -627,7 +628,8 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s) {
 
   timer_begin("fa_bwd_dq", s);
   if (a.d == 128) {
-    if (drop) bwd_dq_kernel<128, TK128, false, false, true><<<grid, block, 0, s>>>(p);
+    // (32-key tiles with dropout: the generator's registers do not fit next to 64-key tiles.)
+    if (drop) bwd_dq_kernel<128, 32, false, false, true><<<grid, block, 0, s>>>(p);
     else if (sparse && smask) bwd_dq_kernel<128, TK128, true, true><<<grid, block, 0, s>>>(p);
     else if (sparse) bwd_dq_kernel<128, TK128, true><<<grid, block, 0, s>>>(p);
     else bwd_dq_kernel<128, TK128, false><<<grid, block, 0, s>>>(p);
