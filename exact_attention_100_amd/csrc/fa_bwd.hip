@@ -91,6 +91,19 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdKParams p) {
 // ------------------------------------------------------------------------------ dK, dV
 
 // Query rows per tile of the dK/dV pass, per head dim.
+// FA_BWD_DKDV_PIPE: the dK/dV tile as one stream of MFMAs with the softmax work in
+// slices between them (1), or as separate product and softmax phases (0).
+// FA_BWD_DKDV_AHEAD_D*: MFMAs whose LDS operands are in flight ahead of their use
+// (one at d = 128, where more does not fit in 256 registers).
+#ifndef FA_BWD_DKDV_PIPE
+#define FA_BWD_DKDV_PIPE 1
+#endif
+#ifndef FA_BWD_DKDV_AHEAD_D128
+#define FA_BWD_DKDV_AHEAD_D128 1
+#endif
+#ifndef FA_BWD_DKDV_AHEAD_D64
+#define FA_BWD_DKDV_AHEAD_D64 2
+#endif
 #ifndef FA_BWD_TILE_Q_D128
 #define FA_BWD_TILE_Q_D128 32
 #endif
@@ -120,6 +133,7 @@ void bwd_dkdv_kernel(BwdKParams p) {
   constexpr int NKK = D / 16;
   constexpr int TILE = BRQ * D;
   static_assert(BRQ <= 64, "row statistics use one 64-lane copy");
+  constexpr bool PIPE = FA_BWD_DKDV_PIPE && !DROP;
 
   // Double buffers as separate arrays, each access naming one statically (the
   // query-tile loop is unrolled by two), so that LDS reads of the current tile
@@ -227,10 +241,6 @@ void bwd_dkdv_kernel(BwdKParams p) {
       // its own tile); every wave finished reading them before the previous barrier.
       issue_tile(tile_q0(min(t + 1, n_qt - 1)), qw, dow, lw, dlw);
 
-      // Dropout keep bits of this tile, bit 16 sb + r for register r of query block sb,
-      // computed before the products while few registers are live: registers
-      // 4 j .. 4 j + 3 are queries qb4 .. qb4 + 3 of this lane's key, i.e. byte
-      // (key mod 4) of words 0..3 at one counter.
       // Dropout keep bits of this tile, bit 16 sb + r for register r of query block sb
       // (registers 4 j .. 4 j + 3 are query quad q0 + 4 g + 8 (4 sb + j)), computed
       // before the products while few registers are live.
@@ -241,6 +251,156 @@ void bwd_dkdv_kernel(BwdKParams p) {
         __builtin_amdgcn_sched_barrier(0);
       }
 
+      // Rows past N carry lse2 = +inf (P = 0) only when they exist in the loaded
+      // statistics, so they are masked too. Masked entries of S become -inf, so that
+      // 2^(c S - lse2) = 0 there (c > 0).
+      const bool need_mask =
+          (!SPARSE || SMASK) && ((p.causal && q0 < kw0 + 31) || (kw0 + 32 > kv_len) || (q0 + BRQ > N));
+      auto mask_scores = [&](f32x16 (&s)[NQB]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int sb = 0; sb < NQB; ++sb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int qi = q0 + 32 * sb + 8 * (r >> 2) + 4 * g + (r & 3);
+            const bool ok = mykey < kv_len && qi < N && (!p.causal || mykey <= qi);
+            if (!ok) s[sb][r] = kNegInf;
+          }
+      };
+
+      if constexpr (PIPE) {
+        // One stream of MFMAs: S (NSM of them), dP (NSM), dV (NVM), dK (NVM). Each
+        // MFMA's LDS operand is an inline-assembly read issued AH MFMAs ahead and
+        // waited for exactly (lds_wait; with copies in flight the compiler would
+        // drain every LDS read before each product). The element work runs in slices
+        // between the MFMAs that do not depend on it: P = 2^(c S - lse2) between
+        // the dP products, dS = P (dP - D) between the dV products, so that each
+        // wave keeps its matrix core busy through its own softmax work.
+        constexpr int NE = 16 * NQB;       // scores per lane
+        constexpr int NG = NE / 4;         // groups of four (one 16-byte read of lse2 or D)
+        constexpr int NSM = NKK * NQB;     // S products (as many dP products)
+        constexpr int NVM = 2 * NQB * NDB; // dV products (as many dK products)
+        constexpr int NM = 2 * NSM + 2 * NVM;
+        constexpr int AH = D == 128 ? FA_BWD_DKDV_AHEAD_D128 : FA_BWD_DKDV_AHEAD_D64;
+        static_assert(!VLDS || NQB == 1, "one V row read per dP product");
+        const uint32_t qbase = lds_address(qr), dobase = lds_address(dor);
+        const uint32_t vbase = VLDS ? lds_address(sV) + (uint32_t)wu * (64 * D) : 0u;
+        const uint32_t lbase = lds_address(lr) + 16 * g, dbase = lds_address(dlr) + 16 * g;
+        // Group G (registers 4 (G % 4) .. + 3 of query block G / 4) is exponentiated
+        // after dP product sP(G) and turned into dS after dV product sD(G); its lse2 and
+        // D are read two MFMAs earlier. Slice 0 of each phase is left out: the first
+        // product's inputs are still in flight.
+        auto sP = [](int G) { return 1 + (G * (NSM - 1)) / NG; };
+        auto sD = [](int G) { return 1 + (G * (NVM - 1)) / NG; };
+        int nrd = 0;  // reads issued so far in this tile (all indices fold to constants)
+        bf16x8 ra[AH + 1], rb[AH + 1];
+        int ia[AH + 1];
+        f32x4 lq[NG], dq[NG];
+        int il[NG], id[NG];
+        auto fetch = [&](int m) __attribute__((always_inline)) {
+          const int s = m % (AH + 1);
+          if (m < NSM) {
+            ra[s] = to.read_row_asm(qbase, m % NQB, m / NQB);
+            nrd += 1;
+          } else if (m < 2 * NSM) {
+            const int j = m - NSM;
+            ra[s] = to.read_row_asm(dobase, j % NQB, j / NQB);
+            nrd += 1;
+            if constexpr (VLDS) {
+              rb[s] = to.read_row_asm(vbase, 0, j);
+              nrd += 1;
+            }
+          } else if (m < 2 * NSM + NVM) {
+            const int i = m - 2 * NSM;
+            ra[s] = to.read_tr_asm(dobase, i / NDB, i % NDB);
+            nrd += 2;
+          } else {
+            const int i = m - 2 * NSM - NVM;
+            ra[s] = to.read_tr_asm(qbase, i / NDB, i % NDB);
+            nrd += 2;
+          }
+          ia[s] = nrd - 1;
+        };
+        auto fetch_stats = [&](int m) __attribute__((always_inline)) {
+#pragma unroll
+          for (int G = 0; G < NG; ++G) {
+            const int off = 128 * (G / 4) + 32 * (G % 4);  // floats 32 sb + 8 j, in bytes
+            if (m == NSM + sP(G) - 2) {
+              lq[G] = lds_read_f32x4_asm(lbase, off);
+              il[G] = nrd++;
+            }
+            if (m == 2 * NSM + sD(G) - 2) {
+              dq[G] = lds_read_f32x4_asm(dbase, off);
+              id[G] = nrd++;
+            }
+          }
+        };
+        f32x16 sacc[NQB], dpacc[NQB];
+#pragma unroll
+        for (int sb = 0; sb < NQB; ++sb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            sacc[sb][r] = 0.f;
+            dpacc[sb][r] = 0.f;
+          }
+        bf16x8 pb[2 * NQB], dsb[2 * NQB];
+#pragma unroll
+        for (int m = 0; m < AH; ++m) fetch(m);
+        static_for<NM>([&](auto mc) __attribute__((always_inline)) {
+          constexpr int m = decltype(mc)::value;
+          if (m + AH < NM) fetch(m + AH);
+          fetch_stats(m);
+          int need = ia[m % (AH + 1)];
+#pragma unroll
+          for (int G = 0; G < NG; ++G) {
+            if (m == NSM + sP(G)) need = il[G] > need ? il[G] : need;
+            if (m == 2 * NSM + sD(G)) need = id[G] > need ? id[G] : need;
+          }
+          lds_wait(nrd - 1 - need);
+          __builtin_amdgcn_sched_barrier(0);
+          const bf16x8 a = ra[m % (AH + 1)];
+          if (m < NSM) {
+            sacc[m % NQB] = mfma_bf16(a, kf[m / NQB], sacc[m % NQB]);
+          } else if (m < 2 * NSM) {
+            const int j = m - NSM;
+            if constexpr (VLDS)
+              dpacc[j % NQB] = mfma_bf16(a, rb[m % (AH + 1)], dpacc[j % NQB]);
+            else
+              dpacc[j % NQB] = mfma_bf16(a, vf[j / NQB], dpacc[j % NQB]);
+            if (j == 0 && need_mask) mask_scores(sacc);
+#pragma unroll
+            for (int G = 0; G < NG; ++G)
+              if (j == sP(G)) {
+                const int sb = G / 4, r0 = 4 * (G % 4);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sacc[sb][r0 + i] = fast_exp2(fmaf(sacc[sb][r0 + i], p.c, -lq[G][i]));
+                if (G & 1) {
+                  const int h = 8 * ((G % 4) / 2);
+                  const f32x16& P = sacc[sb];
+                  pb[G / 2] = pack_bf16x8(P[h], P[h + 1], P[h + 2], P[h + 3], P[h + 4], P[h + 5], P[h + 6], P[h + 7]);
+                }
+              }
+          } else if (m < 2 * NSM + NVM) {
+            const int i = m - 2 * NSM;
+            dvacc[i % NDB] = mfma_bf16(a, pb[i / NDB], dvacc[i % NDB]);
+#pragma unroll
+            for (int G = 0; G < NG; ++G)
+              if (i == sD(G)) {
+                const int sb = G / 4, r0 = 4 * (G % 4);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) dpacc[sb][r0 + k] = sacc[sb][r0 + k] * (dpacc[sb][r0 + k] - dq[G][k]);
+                if (G & 1) {
+                  const int h = 8 * ((G % 4) / 2);
+                  const f32x16& S = dpacc[sb];
+                  dsb[G / 2] = pack_bf16x8(S[h], S[h + 1], S[h + 2], S[h + 3], S[h + 4], S[h + 5], S[h + 6], S[h + 7]);
+                }
+              }
+          } else {
+            const int i = m - 2 * NSM - NVM;
+            dkacc[i % NDB] = mfma_bf16(a, dsb[i / NDB], dkacc[i % NDB]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        });
+      } else {
       // S = Q_i K_w^T and dP = dO_i V_w^T (rows = queries, columns = this wave's keys).
       f32x16 sacc[NQB], dpacc[NQB];
 #pragma unroll
@@ -264,21 +424,8 @@ void bwd_dkdv_kernel(BwdKParams p) {
         }
 
       // P = 2^(c S - lse2), dS = P (dP - D). Register r of sub-block sb is query
-      // q0 + 32 sb + 8 (r/4) + 4 g + r%4. Rows past N carry lse2 = +inf (P = 0)
-      // only when they exist in the loaded statistics, so they are masked too.
-      const bool need_mask =
-          (!SPARSE || SMASK) && ((p.causal && q0 < kw0 + 31) || (kw0 + 32 > kv_len) || (q0 + BRQ > N));
-      // Masked entries of S become -inf, so that 2^(c S - lse2) = 0 there (c > 0).
-      if (need_mask) {
-#pragma unroll
-        for (int sb = 0; sb < NQB; ++sb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int qi = q0 + 32 * sb + 8 * (r >> 2) + 4 * g + (r & 3);
-            const bool ok = mykey < kv_len && qi < N && (!p.causal || mykey <= qi);
-            if (!ok) sacc[sb][r] = kNegInf;
-          }
-      }
+      // q0 + 32 sb + 8 (r/4) + 4 g + r%4.
+      if (need_mask) mask_scores(sacc);
 #pragma unroll
       for (int sb = 0; sb < NQB; ++sb)
 #pragma unroll
@@ -328,6 +475,7 @@ void bwd_dkdv_kernel(BwdKParams p) {
           dvacc[db] = mfma_bf16(to.read_tr(dor, qs, db), pb[qs], dvacc[db]);
           dkacc[db] = mfma_bf16(to.read_tr(qr, qs, db), dsb[qs], dkacc[db]);
         }
+      }
 
       wait_vmem();
       __syncthreads();

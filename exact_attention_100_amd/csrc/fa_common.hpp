@@ -16,6 +16,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 namespace fa {
 
 typedef __bf16 bf16;
@@ -233,6 +235,34 @@ __device__ __forceinline__ bf16x4 lds_read_tr_asm(uint32_t addr, int off) {
   return __builtin_bit_cast(bf16x4, v);
 }
 // s_waitcnt lgkmcnt(n) (vmcnt and expcnt left alone); n must fold to a constant.
+// Calls f(std::integral_constant<int, i>) for i = 0 .. N - 1 in order: a loop whose
+// index is a compile-time constant in the body, whatever the body's size.
+template <class F, int... Is>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Four consecutive floats of a per-row statistics vector (LDS), as inline assembly
+// like the tile reads; off is one of the row-group offsets below.
+#define FA_DS_STAT_OFFSETS(X) X(0) X(32) X(64) X(96) X(128) X(160) X(192) X(224)
+__device__ __forceinline__ f32x4 lds_read_f32x4_asm(uint32_t addr, int off) {
+  f32x4 v;
+  switch (off) {
+#define FA_CASE(O) \
+  case O:          \
+    asm volatile("ds_read_b128 %0, %1 offset:" #O : "=v"(v) : "v"(addr)); \
+    break;
+    FA_DS_STAT_OFFSETS(FA_CASE)
+#undef FA_CASE
+    default:
+      asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr + off));
+  }
+  return v;
+}
 __device__ __forceinline__ void lds_wait(int n) {
   switch (n) {
 #define FA_W(N) \
