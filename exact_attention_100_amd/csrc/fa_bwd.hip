@@ -372,7 +372,10 @@ void bwd_dkdv_kernel(BwdKParams p) {
               if (j == sP(G)) {
                 const int sb = G / 4, r0 = 4 * (G % 4);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) sacc[sb][r0 + i] = fast_exp2(fmaf(sacc[sb][r0 + i], p.c, -lq[G][i]));
+                for (int i = 0; i < 4; ++i) {
+                  sacc[sb][r0 + i] = fast_exp2(fmaf(sacc[sb][r0 + i], p.c, -lq[G][i]));
+                  asm volatile("" : "+v"(sacc[sb][r0 + i]));  // keeps the slice here
+                }
                 if (G & 1) {
                   const int h = 8 * ((G % 4) / 2);
                   const f32x16& P = sacc[sb];
@@ -392,6 +395,7 @@ void bwd_dkdv_kernel(BwdKParams p) {
                   const int h = 8 * ((G % 4) / 2);
                   const f32x16& S = dpacc[sb];
                   dsb[G / 2] = pack_bf16x8(S[h], S[h + 1], S[h + 2], S[h + 3], S[h + 4], S[h + 5], S[h + 6], S[h + 7]);
+                  asm volatile("" : "+v"(dsb[G / 2]));
                 }
               }
           } else {
@@ -512,6 +516,17 @@ void bwd_dkdv_kernel(BwdKParams p) {
 #ifndef FA_BWD_TILE_K_D128
 #define FA_BWD_TILE_K_D128 64
 #endif
+// FA_BWD_DQ_PIPE: the dQ tile as one stream of MFMAs with the P and dS work in slices
+// between them (1), or as separate product and element phases (0).
+#ifndef FA_BWD_DQ_PIPE
+#define FA_BWD_DQ_PIPE 1
+#endif
+#ifndef FA_BWD_DQ_AHEAD_D128
+#define FA_BWD_DQ_AHEAD_D128 1
+#endif
+#ifndef FA_BWD_DQ_AHEAD_D64
+#define FA_BWD_DQ_AHEAD_D64 2
+#endif
 #ifndef FA_BWD_TILE_K_D64
 #define FA_BWD_TILE_K_D64 64
 #endif
@@ -531,6 +546,7 @@ void bwd_dq_kernel(BwdKParams p) {
   constexpr int NDB = D / 32;
   constexpr int NKK = D / 16;
   constexpr int TILE = BC * D;
+  constexpr bool PIPE = FA_BWD_DQ_PIPE && !DROP && NKB == 2;
 
   // Double buffers as separate arrays, named statically (the key-tile loop is
   // unrolled by two) so that reads of the current tile do not wait for the
@@ -614,7 +630,18 @@ void bwd_dq_kernel(BwdKParams p) {
     to.refresh();
     issue_tile(tile_kv0(min(t + 1, n_tiles - 1)), kw, vw);
 
-    // S^T and dP^T (keys x queries).
+    // dS^T = P^T (dP^T - D); register r of block kb is key kv0 + 32 kb + 8 (r/4) + 4 g + r%4.
+    const bool need_mask = (!SPARSE || SMASK) && ((kv0 + BC > kv_len) || (p.causal && kv0 + BC - 1 > q0 + 32 * wave));
+    // Masked entries of S become -inf, so that 2^(c S - lse2) = 0 there (c > 0).
+    auto mask_block = [&](f32x16& s, int kb) __attribute__((always_inline)) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = kv0 + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
+        const bool ok = key < kv_len && (!p.causal || key <= qrow);
+        if (!ok) s[r] = kNegInf;
+      }
+    };
+
     f32x16 sacc[NKB], dpacc[NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
@@ -623,6 +650,95 @@ void bwd_dq_kernel(BwdKParams p) {
         sacc[kb][r] = 0.f;
         dpacc[kb][r] = 0.f;
       }
+
+    if constexpr (PIPE) {
+      // One stream of MFMAs per tile, key block by key block: S^T of blocks 0 and 1
+      // (NKK each), dP^T of blocks 0 and 1, then dQ (NQM). LDS operands are
+      // inline-assembly reads issued AH MFMAs ahead and waited for exactly. The
+      // element work of a block starts one MFMA after the products it needs:
+      // P of block 0 between the S products of block 1, P of block 1 between the dP
+      // products of block 0, dS of block 0 between those of block 1, and dS of
+      // block 1 between the first half of the dQ products (which use block 0 only).
+      constexpr int NS = NKK * NKB;            // S products (as many dP products)
+      constexpr int NQM = (BC / 16) * NDB;     // dQ products
+      constexpr int NM = 2 * NS + NQM;
+      constexpr int AH = D == 128 ? FA_BWD_DQ_AHEAD_D128 : FA_BWD_DQ_AHEAD_D64;
+      const uint32_t kbase = lds_address(kr), vbase = lds_address(vr);
+      int nrd = 0;  // reads issued so far in this tile (folds to constants)
+      bf16x8 ra[AH + 1];
+      int ia[AH + 1];
+      auto fetch = [&](int m) __attribute__((always_inline)) {
+        const int s = m % (AH + 1);
+        if (m < NS) {
+          ra[s] = to.read_row_asm(kbase, m / NKK, m % NKK);
+          nrd += 1;
+        } else if (m < 2 * NS) {
+          ra[s] = to.read_row_asm(vbase, (m - NS) / NKK, (m - NS) % NKK);
+          nrd += 1;
+        } else {
+          const int i = m - 2 * NS;
+          ra[s] = to.read_tr_asm(kbase, i / NDB, i % NDB);
+          nrd += 2;
+        }
+        ia[s] = nrd - 1;
+      };
+      // Element windows [w0, w0 + len) of MFMA indices and the share of slot m in it.
+      auto share = [](int m, int w0, int len, int& e0, int& e1) {
+        const int k = m - w0;
+        e0 = (k >= 0 && k < len) ? (k * 16) / len : 0;
+        e1 = (k >= 0 && k < len) ? ((k + 1) * 16) / len : 0;
+      };
+      bf16x8 dsb[2 * NKB];
+#pragma unroll
+      for (int m = 0; m < AH; ++m) fetch(m);
+      static_for<NM>([&](auto mc) __attribute__((always_inline)) {
+        constexpr int m = decltype(mc)::value;
+        if (m + AH < NM) fetch(m + AH);
+        lds_wait(nrd - 1 - ia[m % (AH + 1)]);
+        __builtin_amdgcn_sched_barrier(0);
+        const bf16x8 a = ra[m % (AH + 1)];
+        if (m < NS)
+          sacc[m / NKK] = mfma_bf16(a, qf[m % NKK], sacc[m / NKK]);
+        else if (m < 2 * NS)
+          dpacc[(m - NS) / NKK] = mfma_bf16(a, df[(m - NS) % NKK], dpacc[(m - NS) / NKK]);
+        else
+          dqacc[(m - 2 * NS) % NDB] = mfma_bf16(a, dsb[(m - 2 * NS) / NDB], dqacc[(m - 2 * NS) % NDB]);
+        // P of block kb over window (first S product of the next block or first dP
+        // product) + 1 .. its end; the mask first when this tile needs it.
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          const int w0 = (kb == 0 ? NKK : NS) + 1, len = NKK - 1;
+          if (m == w0 && need_mask) mask_block(sacc[kb], kb);
+          int e0, e1;
+          share(m, w0, len, e0, e1);
+#pragma unroll
+          for (int e = e0; e < e1; ++e) {
+            sacc[kb][e] = fast_exp2(fmaf(sacc[kb][e], p.c, -lse2_q));
+            asm volatile("" : "+v"(sacc[kb][e]));  // keeps the slice here (no sinking to its use)
+          }
+        }
+        // dS of block kb: block 0 between the dP products of block 1, block 1
+        // between the dQ products of the first half.
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          const int w0 = (kb == 0 ? NS + NKK : 2 * NS) + 1, len = kb == 0 ? NKK - 1 : NQM / 2 - 1;
+          int e0, e1;
+          share(m, w0, len, e0, e1);
+#pragma unroll
+          for (int e = e0; e < e1; ++e) {
+            dpacc[kb][e] = sacc[kb][e] * (dpacc[kb][e] - d_q);
+            if ((e & 7) == 7) {
+              const int h = e - 7;
+              const f32x16& S = dpacc[kb];
+              dsb[2 * kb + h / 8] = pack_bf16x8(S[h], S[h + 1], S[h + 2], S[h + 3], S[h + 4], S[h + 5], S[h + 6], S[h + 7]);
+              asm volatile("" : "+v"(dsb[2 * kb + h / 8]));
+            }
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    } else {
+    // S^T and dP^T (keys x queries).
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
@@ -631,19 +747,9 @@ void bwd_dq_kernel(BwdKParams p) {
         dpacc[kb] = mfma_bf16(to.read_row(vr, kb, kk), df[kk], dpacc[kb]);
       }
 
-    // dS^T = P^T (dP^T - D); register r of block kb is key kv0 + 32 kb + 8 (r/4) + 4 g + r%4.
-    const bool need_mask = (!SPARSE || SMASK) && ((kv0 + BC > kv_len) || (p.causal && kv0 + BC - 1 > q0 + 32 * wave));
-    // Masked entries of S become -inf, so that 2^(c S - lse2) = 0 there (c > 0).
-    if (need_mask) {
+    if (need_mask)
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kv0 + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
-          const bool ok = key < kv_len && (!p.causal || key <= qrow);
-          if (!ok) sacc[kb][r] = kNegInf;
-        }
-    }
+      for (int kb = 0; kb < NKB; ++kb) mask_block(sacc[kb], kb);
     // Dropout: registers 4 q4 .. 4 q4 + 3 of block kb are key quad c = 4 kb + q4
     // (keys kv0 + 4 g + 8 c .. + 3) of this lane's query.
     uint32_t dw[4 * NKB];
@@ -683,6 +789,7 @@ void bwd_dq_kernel(BwdKParams p) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
         dqacc[db] = mfma_bf16(to.read_tr(kr, ks, db), dsb[ks], dqacc[db]);
+    }
 
     wait_vmem();
     __syncthreads();
