@@ -168,6 +168,86 @@ def cpu_baseline(case, budget_s: float):
                       f"at full N={case.N}, d={case.d}; {el:.1f} s wall"}
 
 
+def standard_attention_step(q, k, v, do, scale: float, causal: bool):
+    """The pages' baseline for the memory / runtime comparison, not part of the path:
+    standard attention as separate framework ops that materialise S and P in HBM
+    (FlashAttention reading notes, Background > Standard Attention Implementation),
+    forward and the analytic backward, bf16 with float32 accumulation inside each
+    product. Every transposed operand is made contiguous before its product."""
+    import torch
+    kt = k.transpose(-1, -2).contiguous()
+    s = torch.matmul(q, kt).mul_(scale)
+    if causal:
+        n = q.shape[-2]
+        s.masked_fill_(torch.ones(n, n, dtype=torch.bool, device=q.device).triu_(1), float("-inf"))
+    p = torch.softmax(s, dim=-1)
+    del s
+    o = torch.matmul(p, v)
+    pt = p.transpose(-1, -2).contiguous()
+    dv = torch.matmul(pt, do)
+    del pt
+    vt = v.transpose(-1, -2).contiguous()
+    ds = torch.matmul(do, vt)  # dP, turned into dS = P (dP - D) in place
+    dd = (do.float() * o.float()).sum(-1, keepdim=True).to(q.dtype)
+    ds.sub_(dd).mul_(p)
+    del p
+    dq = torch.matmul(ds, k).mul_(scale)
+    dst = ds.transpose(-1, -2).contiguous()
+    del ds
+    dk = torch.matmul(dst, q).mul_(scale)
+    return o, dq, dk, dv
+
+
+def memory_sweep(ns, B: int = 1, H: int = 16, d: int = 64, reps: int = 3):
+    """Peak device memory and time of one causal fwd + bwd step over N, for this
+    path and for standard attention (the pages' memory-footprint and runtime
+    benchmark, Experiments > 4.4; Theorem 1: extra memory O(N)). One JSON line per
+    N; memory is the peak above the four resident inputs."""
+    import numpy as np
+    import torch
+
+    import exact_attention_100_amd as fa
+    import workloads
+    dev = torch.device("cuda:0")
+    for n in ns:
+        case = workloads.make_case(B, H, n, d, dtype=workloads.BF16, mask="causal", seed=100 + n.bit_length())
+        t = {x: torch.from_numpy(case.bits(x).view(np.int16)).view(torch.bfloat16).to(dev)
+             for x in ("q", "k", "v", "do")}
+        sc = float(case.scale)
+        row = {"N": n, "B": B, "H": H, "d": d, "mask": "causal"}
+        for name in ("flash", "standard"):
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
+            base = torch.cuda.memory_allocated(dev)
+            torch.cuda.reset_peak_memory_stats(dev)
+            try:
+                def step():
+                    if name == "flash":
+                        o, lse = fa.fwd(t["q"], t["k"], t["v"], scale=sc, causal=True)
+                        return fa.bwd(t["q"], t["k"], t["v"], o, t["do"], lse, scale=sc, causal=True)
+                    return standard_attention_step(t["q"], t["k"], t["v"], t["do"], sc, True)
+                step()
+                torch.cuda.synchronize()
+                peak = torch.cuda.max_memory_allocated(dev) - base
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(reps):
+                    step()
+                e1.record()
+                torch.cuda.synchronize()
+                row[name] = {"peak_extra_bytes": int(peak), "ms_per_step": round(e0.elapsed_time(e1) / reps, 4)}
+            except torch.cuda.OutOfMemoryError:
+                row[name] = "out of memory"
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
+        f, s = row["flash"], row["standard"]
+        if isinstance(f, dict) and isinstance(s, dict):
+            row["standard_over_flash"] = {"memory": round(s["peak_extra_bytes"] / f["peak_extra_bytes"], 2),
+                                          "time": round(s["ms_per_step"] / f["ms_per_step"], 2)}
+        print(json.dumps(row), flush=True)
+        del t
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -184,7 +264,13 @@ def main():
     ap.add_argument("--digest-counters", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
                                                            "COPY_WRITE_DIR"),
                     help="print per-kernel HBM traffic from rocprofv3 --pmc csv runs")
+    ap.add_argument("--memory-sweep", nargs="*", type=int, metavar="N",
+                    help="peak memory and time of this path and of standard attention over N "
+                         "(B=1, H=16, d=64, causal; default N = 1K .. 64K)")
     args = ap.parse_args()
+    if args.memory_sweep is not None:
+        memory_sweep(args.memory_sweep or [1 << e for e in range(10, 17)])
+        return
     if args.digest_counters:
         digest_counters(*args.digest_counters, workload=args.workload)
         return
