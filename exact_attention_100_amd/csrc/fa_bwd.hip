@@ -267,7 +267,13 @@ void bwd_dkdv_kernel(BwdKParams p) {
           }
       };
 
+      // A wave whose keys all follow this tile's queries (causal) or lie past kv_len
+      // has P = 0 on the whole tile: its products would add nothing, so it skips them
+      // (it still issues its share of the copies and meets the barrier).
+      const int kw0u = k0 + 32 * wu;
+      const bool idle = (!SPARSE || SMASK) && ((p.causal && q0 + BRQ - 1 < kw0u) || kw0u >= kv_len);
       if constexpr (PIPE) {
+        if (!idle) {
         // One stream of MFMAs: S (NSM of them), dP (NSM), dV (NVM), dK (NVM). Each
         // MFMA's LDS operand is an inline-assembly read issued AH MFMAs ahead and
         // waited for exactly (lds_wait; with copies in flight the compiler would
@@ -404,6 +410,7 @@ void bwd_dkdv_kernel(BwdKParams p) {
           }
           __builtin_amdgcn_sched_barrier(0);
         });
+        }
       } else {
       // S = Q_i K_w^T and dP = dO_i V_w^T (rows = queries, columns = this wave's keys).
       f32x16 sacc[NQB], dpacc[NQB];
@@ -651,7 +658,13 @@ void bwd_dq_kernel(BwdKParams p) {
         dpacc[kb][r] = 0.f;
       }
 
+    // A wave whose queries all precede this tile's keys (causal), or a tile past
+    // kv_len, has P = 0 everywhere: the wave skips its products (not the copies or
+    // the barrier).
+    const int wq = uniform_wave_id();
+    const bool idle = (!SPARSE || SMASK) && ((p.causal && kv0 > q0 + 32 * wq + 31) || kv0 >= kv_len);
     if constexpr (PIPE) {
+      if (!idle) {
       // One stream of MFMAs per tile, key block by key block: S^T of blocks 0 and 1
       // (NKK each), dP^T of blocks 0 and 1, then dQ (NQM). LDS operands are
       // inline-assembly reads issued AH MFMAs ahead and waited for exactly. The
@@ -737,6 +750,7 @@ void bwd_dq_kernel(BwdKParams p) {
         }
         __builtin_amdgcn_sched_barrier(0);
       });
+      }
     } else {
     // S^T and dP^T (keys x queries).
 #pragma unroll
