@@ -135,13 +135,21 @@ void bwd_dkdv_kernel(BwdKParams p) {
   static_assert(BRQ <= 64, "row statistics use one 64-lane copy");
   constexpr bool PIPE = FA_BWD_DKDV_PIPE && !DROP;
 
-  // Double buffers as separate arrays, each access naming one statically (the
-  // query-tile loop is unrolled by two), so that LDS reads of the current tile
-  // do not wait for the copies of the next tile still in flight.
-  __shared__ __attribute__((aligned(16))) bf16 sQ0[TILE];
-  __shared__ __attribute__((aligned(16))) bf16 sQ1[TILE];
-  __shared__ __attribute__((aligned(16))) bf16 sdO0[TILE];
-  __shared__ __attribute__((aligned(16))) bf16 sdO1[TILE];
+  // Double buffers. The pipelined tile reads them only through inline assembly, so
+  // they share one array [Q0 | dO0 | Q1 | dO1]: each lane's read addresses are then
+  // computed once and a read names its buffer by the instruction's immediate offset.
+  // The phased tile reads them with compiler loads and keeps separate arrays, each
+  // access naming one statically (the loop is unrolled by two), so that reads of the
+  // current tile do not wait for the copies of the next tile still in flight.
+  __shared__ __attribute__((aligned(16))) bf16 sT[PIPE ? 4 * TILE : 8];
+  __shared__ __attribute__((aligned(16))) bf16 sQ0[PIPE ? 8 : TILE];
+  __shared__ __attribute__((aligned(16))) bf16 sQ1[PIPE ? 8 : TILE];
+  __shared__ __attribute__((aligned(16))) bf16 sdO0[PIPE ? 8 : TILE];
+  __shared__ __attribute__((aligned(16))) bf16 sdO1[PIPE ? 8 : TILE];
+  bf16* const bQ0 = PIPE ? sT : sQ0;
+  bf16* const bdO0 = PIPE ? sT + TILE : sdO0;
+  bf16* const bQ1 = PIPE ? sT + 2 * TILE : sQ1;
+  bf16* const bdO1 = PIPE ? sT + 3 * TILE : sdO1;
   __shared__ __attribute__((aligned(16))) float sL0[64];
   __shared__ __attribute__((aligned(16))) float sL1[64];
   __shared__ __attribute__((aligned(16))) float sDl0[64];
@@ -220,6 +228,8 @@ void bwd_dkdv_kernel(BwdKParams p) {
     cp.init(wu, lane, p.sn);
     TileOffsets<D> to;
     to.init(lane);
+    TileAddr<D> ta;  // (the pipelined tile's addresses in sT)
+    ta.init(to, lds_address(sT));
     auto issue_tile = [&](int q0, bf16* qw, bf16* dow, float* lw, float* dlw) __attribute__((always_inline)) {
       cp.issue(qw, Qh, p.sn, q0, N);
       cp.issue(dow, dOh, p.sn, q0, N);
@@ -227,7 +237,7 @@ void bwd_dkdv_kernel(BwdKParams p) {
       if (wave == 1) vec_dma64(dlw, p.delta + rowbase, q0, N, lane);
     };
 
-    issue_tile(tile_q0(0), sQ0, sdO0, sL0, sDl0);
+    issue_tile(tile_q0(0), bQ0, bdO0, sL0, sDl0);
     wait_vmem();
     __syncthreads();
 
@@ -236,7 +246,7 @@ void bwd_dkdv_kernel(BwdKParams p) {
     auto iteration = [&](int t, const bf16* qr, const bf16* dor, const float* lr, const float* dlr, bf16* qw,
                          bf16* dow, float* lw, float* dlw) __attribute__((always_inline)) {
       const int q0 = tile_q0(t);
-      to.refresh();
+      if constexpr (!PIPE) to.refresh();
       // Prefetch the next tile into the idle buffers (the last iteration re-reads
       // its own tile); every wave finished reading them before the previous barrier.
       issue_tile(tile_q0(min(t + 1, n_qt - 1)), qw, dow, lw, dlw);
@@ -288,8 +298,11 @@ void bwd_dkdv_kernel(BwdKParams p) {
         constexpr int NM = 2 * NSM + 2 * NVM;
         constexpr int AH = D == 128 ? FA_BWD_DKDV_AHEAD_D128 : FA_BWD_DKDV_AHEAD_D64;
         static_assert(!VLDS || NQB == 1, "one V row read per dP product");
-        const uint32_t qbase = lds_address(qr), dobase = lds_address(dor);
-        const uint32_t vbase = VLDS ? lds_address(sV) + (uint32_t)wu * (64 * D) : 0u;
+        // Byte offsets of this tile's buffers in sT (constants once the loop is unrolled).
+        const int qoff = (int)(lds_address(qr) - lds_address(sT)), dooff = (int)(lds_address(dor) - lds_address(sT));
+        uint32_t vdelta = VLDS ? lds_address(sV) - lds_address(sT) + (uint32_t)wu * (64 * D) : 0u;
+        // (opaque per tile, so that the V row addresses are not hoisted into registers)
+        asm volatile("" : "+s"(vdelta));
         const uint32_t lbase = lds_address(lr) + 16 * g, dbase = lds_address(dlr) + 16 * g;
         // Group G (registers 4 (G % 4) .. + 3 of query block G / 4) is exponentiated
         // after dP product sP(G) and turned into dS after dV product sD(G); its lse2 and
@@ -305,23 +318,23 @@ void bwd_dkdv_kernel(BwdKParams p) {
         auto fetch = [&](int m) __attribute__((always_inline)) {
           const int s = m % (AH + 1);
           if (m < NSM) {
-            ra[s] = to.read_row_asm(qbase, m % NQB, m / NQB);
+            ra[s] = ta.read_row(qoff, m % NQB, m / NQB);
             nrd += 1;
           } else if (m < 2 * NSM) {
             const int j = m - NSM;
-            ra[s] = to.read_row_asm(dobase, j % NQB, j / NQB);
+            ra[s] = ta.read_row(dooff, j % NQB, j / NQB);
             nrd += 1;
             if constexpr (VLDS) {
-              rb[s] = to.read_row_asm(vbase, 0, j);
+              rb[s] = lds_read_b128_asm(ta.row[j] + vdelta, 0);  // the wave's V rows
               nrd += 1;
             }
           } else if (m < 2 * NSM + NVM) {
             const int i = m - 2 * NSM;
-            ra[s] = to.read_tr_asm(dobase, i / NDB, i % NDB);
+            ra[s] = ta.read_tr(dooff, i / NDB, i % NDB);
             nrd += 2;
           } else {
             const int i = m - 2 * NSM - NVM;
-            ra[s] = to.read_tr_asm(qbase, i / NDB, i % NDB);
+            ra[s] = ta.read_tr(qoff, i / NDB, i % NDB);
             nrd += 2;
           }
           ia[s] = nrd - 1;
@@ -492,8 +505,8 @@ void bwd_dkdv_kernel(BwdKParams p) {
       __syncthreads();
     };
     for (int t = 0; t < n_qt; t += 2) {
-      iteration(t, sQ0, sdO0, sL0, sDl0, sQ1, sdO1, sL1, sDl1);
-      if (t + 1 < n_qt) iteration(t + 1, sQ1, sdO1, sL1, sDl1, sQ0, sdO0, sL0, sDl0);
+      iteration(t, bQ0, bdO0, sL0, sDl0, bQ1, bdO1, sL1, sDl1);
+      if (t + 1 < n_qt) iteration(t + 1, bQ1, bdO1, sL1, sDl1, bQ0, bdO0, sL0, sDl0);
     }
   }
 
@@ -555,13 +568,19 @@ void bwd_dq_kernel(BwdKParams p) {
   constexpr int TILE = BC * D;
   constexpr bool PIPE = FA_BWD_DQ_PIPE && !DROP && NKB == 2;
 
-  // Double buffers as separate arrays, named statically (the key-tile loop is
-  // unrolled by two) so that reads of the current tile do not wait for the
-  // copies of the next.
-  __shared__ __attribute__((aligned(16))) bf16 sK0[TILE];
-  __shared__ __attribute__((aligned(16))) bf16 sK1[TILE];
-  __shared__ __attribute__((aligned(16))) bf16 sV0[TILE];
-  __shared__ __attribute__((aligned(16))) bf16 sV1[TILE];
+  // Double buffers: one array [K0 | V0 | K1 | V1] for the pipelined tile (inline-assembly
+  // reads, the buffer named by the immediate offset); separate arrays named statically
+  // for the phased tile (the key-tile loop is unrolled by two), so that its compiler
+  // reads of the current tile do not wait for the copies of the next.
+  __shared__ __attribute__((aligned(16))) bf16 sT[PIPE ? 4 * TILE : 8];
+  __shared__ __attribute__((aligned(16))) bf16 sK0[PIPE ? 8 : TILE];
+  __shared__ __attribute__((aligned(16))) bf16 sK1[PIPE ? 8 : TILE];
+  __shared__ __attribute__((aligned(16))) bf16 sV0[PIPE ? 8 : TILE];
+  __shared__ __attribute__((aligned(16))) bf16 sV1[PIPE ? 8 : TILE];
+  bf16* const bK0 = PIPE ? sT : sK0;
+  bf16* const bV0 = PIPE ? sT + TILE : sV0;
+  bf16* const bK1 = PIPE ? sT + 2 * TILE : sK1;
+  bf16* const bV1 = PIPE ? sT + 3 * TILE : sV1;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5;
@@ -623,18 +642,20 @@ void bwd_dq_kernel(BwdKParams p) {
   cp.init(uniform_wave_id(), lane, p.sn);
   TileOffsets<D> to;
   to.init(lane);
+  TileAddr<D> ta;  // (the pipelined tile's addresses in sT)
+  ta.init(to, lds_address(sT));
   auto issue_tile = [&](int kv0, bf16* kw, bf16* vw) __attribute__((always_inline)) {
     cp.issue(kw, Kh, p.sn, kv0, N);
     cp.issue(vw, Vh, p.sn, kv0, N);
   };
-  issue_tile(tile_kv0(0), sK0, sV0);
+  issue_tile(tile_kv0(0), bK0, bV0);
   wait_vmem();
   __syncthreads();
 
   // Iteration t reads tile t from (kr, vr) and copies tile t + 1 into (kw, vw).
   auto iteration = [&](int t, const bf16* kr, const bf16* vr, bf16* kw, bf16* vw) __attribute__((always_inline)) {
     const int kv0 = tile_kv0(t);
-    to.refresh();
+    if constexpr (!PIPE) to.refresh();
     issue_tile(tile_kv0(min(t + 1, n_tiles - 1)), kw, vw);
 
     // dS^T = P^T (dP^T - D); register r of block kb is key kv0 + 32 kb + 8 (r/4) + 4 g + r%4.
@@ -676,21 +697,22 @@ void bwd_dq_kernel(BwdKParams p) {
       constexpr int NQM = (BC / 16) * NDB;     // dQ products
       constexpr int NM = 2 * NS + NQM;
       constexpr int AH = D == 128 ? FA_BWD_DQ_AHEAD_D128 : FA_BWD_DQ_AHEAD_D64;
-      const uint32_t kbase = lds_address(kr), vbase = lds_address(vr);
+      // Byte offsets of this tile's buffers in sT (constants once the loop is unrolled).
+      const int koff = (int)(lds_address(kr) - lds_address(sT)), voff = (int)(lds_address(vr) - lds_address(sT));
       int nrd = 0;  // reads issued so far in this tile (folds to constants)
       bf16x8 ra[AH + 1];
       int ia[AH + 1];
       auto fetch = [&](int m) __attribute__((always_inline)) {
         const int s = m % (AH + 1);
         if (m < NS) {
-          ra[s] = to.read_row_asm(kbase, m / NKK, m % NKK);
+          ra[s] = ta.read_row(koff, m / NKK, m % NKK);
           nrd += 1;
         } else if (m < 2 * NS) {
-          ra[s] = to.read_row_asm(vbase, (m - NS) / NKK, (m - NS) % NKK);
+          ra[s] = ta.read_row(voff, (m - NS) / NKK, (m - NS) % NKK);
           nrd += 1;
         } else {
           const int i = m - 2 * NS;
-          ra[s] = to.read_tr_asm(kbase, i / NDB, i % NDB);
+          ra[s] = ta.read_tr(koff, i / NDB, i % NDB);
           nrd += 2;
         }
         ia[s] = nrd - 1;
@@ -809,8 +831,8 @@ void bwd_dq_kernel(BwdKParams p) {
     __syncthreads();
   };
   for (int t = 0; t < n_tiles; t += 2) {
-    iteration(t, sK0, sV0, sK1, sV1);
-    if (t + 1 < n_tiles) iteration(t + 1, sK1, sV1, sK0, sV0);
+    iteration(t, bK0, bV0, bK1, bV1);
+    if (t + 1 < n_tiles) iteration(t + 1, bK1, bV1, bK0, bV0);
   }
 
   // dQ = scale dQ^T^T: lane = query, register r = dim 32 db + 8 (r/4) + 4 g + r%4.

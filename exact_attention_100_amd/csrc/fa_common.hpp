@@ -205,7 +205,16 @@ struct TileCopy {
 __device__ __forceinline__ uint32_t lds_address(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
 }
-#define FA_DS_OFFSETS(X) X(0) X(1024) X(2048) X(3072) X(4096) X(6144) X(8192) X(12288) X(16384) X(24576)
+// Every multiple of 1 KiB the 16-bit offset field holds (buffer + block offsets of the tile reads).
+#define FA_DS_OFFSETS(X) \
+  X(0) X(1024) X(2048) X(3072) X(4096) X(5120) X(6144) X(7168) \
+  X(8192) X(9216) X(10240) X(11264) X(12288) X(13312) X(14336) X(15360) \
+  X(16384) X(17408) X(18432) X(19456) X(20480) X(21504) X(22528) X(23552) \
+  X(24576) X(25600) X(26624) X(27648) X(28672) X(29696) X(30720) X(31744) \
+  X(32768) X(33792) X(34816) X(35840) X(36864) X(37888) X(38912) X(39936) \
+  X(40960) X(41984) X(43008) X(44032) X(45056) X(46080) X(47104) X(48128) \
+  X(49152) X(50176) X(51200) X(52224) X(53248) X(54272) X(55296) X(56320) \
+  X(57344) X(58368) X(59392) X(60416) X(61440) X(62464) X(63488) X(64512)
 __device__ __forceinline__ bf16x8 lds_read_b128_asm(uint32_t addr, int off) {
   u32x4 v;
   switch (off) {
@@ -329,6 +338,32 @@ struct TileOffsets {
     const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + tr_lo[mb]));
     const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + tr_hi[mb]));
     return concat_bf16x4(lo, hi);
+  }
+};
+
+// The same per-lane offsets with one LDS array's address already added (computed once):
+// reads of the tile buffers inside that array then name the buffer through the
+// instruction's immediate offset only, so no address arithmetic is repeated per tile.
+template <int COLS>
+struct TileAddr {
+  uint32_t row[COLS / 16];
+  uint32_t tr_lo[COLS / 32], tr_hi[COLS / 32];
+  __device__ __forceinline__ void init(const TileOffsets<COLS>& to, uint32_t array_base) {
+#pragma unroll
+    for (int i = 0; i < COLS / 16; ++i) row[i] = array_base + (uint32_t)to.row[i];
+#pragma unroll
+    for (int i = 0; i < COLS / 32; ++i) {
+      tr_lo[i] = array_base + (uint32_t)to.tr_lo[i];
+      tr_hi[i] = array_base + (uint32_t)to.tr_hi[i];
+    }
+  }
+  // buf: byte offset of the tile buffer in the array (folds to a constant).
+  __device__ __forceinline__ bf16x8 read_row(int buf, int b, int kk) const {
+    return lds_read_b128_asm(row[kk], buf + b * 64 * COLS);
+  }
+  __device__ __forceinline__ bf16x8 read_tr(int buf, int ks, int mb) const {
+    return concat_bf16x4(lds_read_tr_asm(tr_lo[mb], buf + 32 * ks * COLS),
+                         lds_read_tr_asm(tr_hi[mb], buf + 32 * ks * COLS));
   }
 };
 

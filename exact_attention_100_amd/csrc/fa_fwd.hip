@@ -204,15 +204,15 @@ void fwd_bf16_kernel(FwdKParams p) {
   constexpr int TILE = BC * D;
 
   // K and V tiles, double-buffered, row-major in the swizzled layout (16-byte
-  // row reads for the K operand, transposing reads for the V^T operand). The
-  // four buffers are separate arrays and every access names one of them
-  // statically (the key loop is unrolled by two): the compiler can then tell
-  // that a read of one buffer does not depend on the direct global -> LDS
-  // copies still in flight into another, and does not wait for them.
-  __shared__ __attribute__((aligned(16))) bf16 sK0[TILE];
-  __shared__ __attribute__((aligned(16))) bf16 sK1[TILE];
-  __shared__ __attribute__((aligned(16))) bf16 sV0[TILE];
-  __shared__ __attribute__((aligned(16))) bf16 sV1[TILE];
+  // row reads for the K operand, transposing reads for the V^T operand), in one
+  // array [K0 | K1 | V0 | V1]. Every read is inline assembly: each lane's
+  // addresses are computed once and a read names its buffer by the instruction's
+  // immediate offset (the key loop is unrolled by two, so those fold).
+  __shared__ __attribute__((aligned(16))) bf16 sT[4 * TILE];
+  bf16* const sK0 = sT;
+  bf16* const sK1 = sT + TILE;
+  bf16* const sV0 = sT + 2 * TILE;
+  bf16* const sV1 = sT + 3 * TILE;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5;
@@ -255,8 +255,12 @@ void fwd_bf16_kernel(FwdKParams p) {
   // predicated).
   TileCopy<BC, D, 4> cp;
   cp.init(uniform_wave_id(), lane, p.sn);
-  TileOffsets<D> to;
-  to.init(lane);
+  TileAddr<D> ta;
+  {
+    TileOffsets<D> to;
+    to.init(lane);
+    ta.init(to, lds_address(sT));
+  }
   const int nt = rg.n_tiles;
   auto kv0_of = [&](int t) { return fwd_tile_kv0<BC, SPARSE>(p, rg, min(t, nt - 1)); };
 
@@ -270,14 +274,14 @@ void fwd_bf16_kernel(FwdKParams p) {
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
-    const uint32_t base = lds_address(sk);
+    const int off = (int)(lds_address(sk) - lds_address(sT));
     bf16x8 ring[kAhead];
 #pragma unroll
-    for (int j = 0; j < kAhead; ++j) ring[j] = to.read_row_asm(base, j % NKB, j / NKB);
+    for (int j = 0; j < kAhead; ++j) ring[j] = ta.read_row(off, j % NKB, j / NKB);
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
       const bf16x8 a = ring[j % kAhead];
-      if (j + kAhead < NS) ring[j % kAhead] = to.read_row_asm(base, (j + kAhead) % NKB, (j + kAhead) / NKB);
+      if (j + kAhead < NS) ring[j % kAhead] = ta.read_row(off, (j + kAhead) % NKB, (j + kAhead) / NKB);
       lds_wait(NS - 1 - j < kAhead ? NS - 1 - j : kAhead);  // the reads issued after operand j
       __builtin_amdgcn_sched_barrier(0);
       sacc[j % NKB] = mfma_bf16(a, qf[j / NKB], sacc[j % NKB]);
@@ -290,7 +294,13 @@ void fwd_bf16_kernel(FwdKParams p) {
 #pragma unroll
     for (int ks = 0; ks < BC / 16; ++ks)
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) oacc[db] = mfma_bf16(to.read_tr(sv, ks, db), pb[ks], oacc[db]);
+      for (int db = 0; db < NDB; ++db) {
+        const bf16x8 a = ta.read_tr((int)(lds_address(sv) - lds_address(sT)), ks, db);
+        lds_wait(0);
+        // (the wait does not order the product by itself: nothing it touches is an operand)
+        __builtin_amdgcn_sched_barrier(0);
+        oacc[db] = mfma_bf16(a, pb[ks], oacc[db]);
+      }
   };
   // Dropout of one tile's packed probabilities (k-step ks = 2 kb + s holds the key
   // quads 32 kb + 16 s + 4 g and that + 8 of this lane's query).
@@ -330,7 +340,6 @@ void fwd_bf16_kernel(FwdKParams p) {
     // Iteration t: K_{t+1} -> kw, V_t -> vw, S(t) from kr, P V of tile t - 1 from vr.
     auto iteration = [&](int t, bf16* kw, const bf16* kr, bf16* vw, const bf16* vr) __attribute__((always_inline)) {
       const int kv0 = kv0_of(t);
-      to.refresh();
       cp.issue(kw, Kh, p.sn, kv0_of(t + 1), N);
       cp.issue(vw, Vh, p.sn, kv0, N);
       f32x16 sacc[NKB];
@@ -347,15 +356,15 @@ void fwd_bf16_kernel(FwdKParams p) {
       constexpr int NEXP = NPV - 3; // slices doing exponentials
       static_assert(NPV >= 4, "too few MFMAs to interleave");
       bf16x8 pbn[2 * NKB];
-      const uint32_t vbase = lds_address(vr);
-      bf16x8 a0 = to.read_tr_asm(vbase, 0, 0);
-      bf16x8 a1 = to.read_tr_asm(vbase, 1 / NDB, 1 % NDB);
+      const int voff = (int)(lds_address(vr) - lds_address(sT));
+      bf16x8 a0 = ta.read_tr(voff, 0, 0);
+      bf16x8 a1 = ta.read_tr(voff, 1 / NDB, 1 % NDB);
       float mx0 = kNegInf, mx1 = kNegInf, m_new = 0.f, m_use = 0.f, alpha = 1.f, rs = 0.f;
 #pragma unroll
       for (int i = 0; i < NPV; ++i) {
         const bf16x8 a = a0;
         a0 = a1;
-        if (i + 2 < NPV) a1 = to.read_tr_asm(vbase, (i + 2) / NDB, (i + 2) % NDB);
+        if (i + 2 < NPV) a1 = ta.read_tr(voff, (i + 2) / NDB, (i + 2) % NDB);
         lds_wait(2 * ((i + 2 < NPV ? i + 2 : NPV - 1) - i));  // two reads per later operand
         __builtin_amdgcn_sched_barrier(0);
         oacc[i % NDB] = mfma_bf16(a, pb[i / NDB], oacc[i % NDB]);
