@@ -133,7 +133,7 @@ void bwd_dkdv_kernel(BwdKParams p) {
   constexpr int NKK = D / 16;
   constexpr int TILE = BRQ * D;
   static_assert(BRQ <= 64, "row statistics use one 64-lane copy");
-  constexpr bool PIPE = FA_BWD_DKDV_PIPE && !DROP;
+  constexpr bool PIPE = FA_BWD_DKDV_PIPE;
 
   // Double buffers. The pipelined tile reads them only through inline assembly, so
   // they share one array [Q0 | dO0 | Q1 | dO1]: each lane's read addresses are then
@@ -255,7 +255,7 @@ void bwd_dkdv_kernel(BwdKParams p) {
       // (registers 4 j .. 4 j + 3 are query quad q0 + 4 g + 8 (4 sb + j)), computed
       // before the products while few registers are live.
       uint32_t keepbits = 0;
-      if (DROP) {
+      if (DROP && !PIPE) {
         keepbits = dropout_col_bits<4 * NQB>(p.drop, mykey, q0 + 4 * g, (uint32_t)inst);
         asm volatile("" : "+v"(keepbits));
         __builtin_amdgcn_sched_barrier(0);
@@ -362,6 +362,7 @@ void bwd_dkdv_kernel(BwdKParams p) {
             dpacc[sb][r] = 0.f;
           }
         bf16x8 pb[2 * NQB], dsb[2 * NQB];
+        Philox rng{};
 #pragma unroll
         for (int m = 0; m < AH; ++m) fetch(m);
         static_for<NM>([&](auto mc) __attribute__((always_inline)) {
@@ -379,6 +380,20 @@ void bwd_dkdv_kernel(BwdKParams p) {
           const bf16x8 a = ra[m % (AH + 1)];
           if (m < NSM) {
             sacc[m % NQB] = mfma_bf16(a, kf[m / NQB], sacc[m % NQB]);
+            if constexpr (DROP) {
+              // Dropout keep bits of the tile (bit 16 sb + r for register r of query block
+              // sb): the generator calls' rounds run between the S products, which carry
+              // no other element work.
+              constexpr int NCALL = NQB;  // one call per four query quads
+              constexpr int NR = 10 * NCALL;
+#pragma unroll
+              for (int r = (m * NR) / NSM; r < ((m + 1) * NR) / NSM; ++r) {
+                const int call = r / 10;
+                if (r % 10 == 0) rng = dropout_col_state(p.drop, mykey, q0 + 4 * g, (uint32_t)inst, 4 * call);
+                rng.round(r % 10);
+                if (r % 10 == 9) keepbits |= dropout_col_bits_of(p.drop, mykey, rng, 4 * call);
+              }
+            }
           } else if (m < 2 * NSM) {
             const int j = m - NSM;
             if constexpr (VLDS)
@@ -398,7 +413,15 @@ void bwd_dkdv_kernel(BwdKParams p) {
                 if (G & 1) {
                   const int h = 8 * ((G % 4) / 2);
                   const f32x16& P = sacc[sb];
-                  pb[G / 2] = pack_bf16x8(P[h], P[h + 1], P[h + 2], P[h + 3], P[h + 4], P[h + 5], P[h + 6], P[h + 7]);
+                  if constexpr (DROP) {
+                    // dV takes P o Z / (1 - p)
+                    float pz[8];
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) pz[k] = ((keepbits >> (16 * sb + h + k)) & 1u) ? P[h + k] * p.drop.scale : 0.f;
+                    pb[G / 2] = pack_bf16x8(pz[0], pz[1], pz[2], pz[3], pz[4], pz[5], pz[6], pz[7]);
+                  } else {
+                    pb[G / 2] = pack_bf16x8(P[h], P[h + 1], P[h + 2], P[h + 3], P[h + 4], P[h + 5], P[h + 6], P[h + 7]);
+                  }
                 }
               }
           } else if (m < 2 * NSM + NVM) {
@@ -409,7 +432,15 @@ void bwd_dkdv_kernel(BwdKParams p) {
               if (i == sD(G)) {
                 const int sb = G / 4, r0 = 4 * (G % 4);
 #pragma unroll
-                for (int k = 0; k < 4; ++k) dpacc[sb][r0 + k] = sacc[sb][r0 + k] * (dpacc[sb][r0 + k] - dq[G][k]);
+                for (int k = 0; k < 4; ++k) {
+                  if constexpr (DROP) {
+                    // dS = P (dP o Z / (1 - p) - D)
+                    const float z = ((keepbits >> (16 * sb + r0 + k)) & 1u) ? p.drop.scale : 0.f;
+                    dpacc[sb][r0 + k] = sacc[sb][r0 + k] * fmaf(dpacc[sb][r0 + k], z, -dq[G][k]);
+                  } else {
+                    dpacc[sb][r0 + k] = sacc[sb][r0 + k] * (dpacc[sb][r0 + k] - dq[G][k]);
+                  }
+                }
                 if (G & 1) {
                   const int h = 8 * ((G % 4) / 2);
                   const f32x16& S = dpacc[sb];

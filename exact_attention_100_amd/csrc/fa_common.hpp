@@ -380,10 +380,11 @@ struct Dropout {
   uint32_t offset;   // counter word 3
   float scale;       // 1 / (1 - p8 / 256)
 };
-__device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
-                                               uint32_t k0, uint32_t k1) {
-#pragma unroll
-  for (int r = 0; r < 10; ++r) {
+// The generator as a state that advances one round at a time, so that its work can be
+// spread over other instructions.
+struct Philox {
+  uint32_t c0, c1, c2, c3, k0, k1;
+  __device__ __forceinline__ void round(int r) {
     if (r) {
       k0 += 0x9E3779B9u;
       k1 += 0xBB67AE85u;
@@ -396,11 +397,17 @@ __device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
     c2 = hi0 ^ c3 ^ k1;
     c3 = lo0;
   }
+};
+__device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                               uint32_t k0, uint32_t k1) {
+  Philox g{c0, c1, c2, c3, k0, k1};
+#pragma unroll
+  for (int r = 0; r < 10; ++r) g.round(r);
   u32x4 r;
-  r[0] = c0;
-  r[1] = c1;
-  r[2] = c2;
-  r[3] = c3;
+  r[0] = g.c0;
+  r[1] = g.c1;
+  r[2] = g.c2;
+  r[3] = g.c3;
   return r;
 }
 // Lane r of each group of four lanes receives v from lane r ^ k (k = 1, 2, 3; DPP).
@@ -443,25 +450,39 @@ __device__ __forceinline__ void dropout_row_words(const Dropout& d, int i, int k
 // 4 m .. 4 m + 3 (j mod 4 = lane mod 4) and need the same calls (one byte of
 // each word), so each lane computes one call in four, reduces it to its 4 x 4
 // keep bits and hands each partner its column. All 64 lanes must be active.
+// The generator state of this lane's call for query quads c0 .. c0 + 3 (see below).
+__device__ __forceinline__ Philox dropout_col_state(const Dropout& d, int j, int q4, uint32_t bh, int c0) {
+  const int t = j & 3;
+  return Philox{(uint32_t)(q4 + 8 * (c0 + t)) >> 2, (uint32_t)j >> 2, bh, d.offset, d.k0, d.k1};
+}
+// Bits 4 c0 .. 4 c0 + 15 of the keep bits below from that call's output words.
+__device__ __forceinline__ uint32_t dropout_col_bits_of(const Dropout& d, int j, const Philox& w, int c0) {
+  const int t = j & 3;
+  const uint32_t wr[4] = {w.c0, w.c1, w.c2, w.c3};
+  uint32_t kb = 0;  // bit 4 b + r: key byte b of query row r kept
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) kb |= (((wr[r] >> (8 * b)) & 0xFFu) >= d.p8 ? 1u : 0u) << (4 * b + r);
+  uint32_t bits = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t send = (kb >> (4 * (t ^ k))) & 0xFu;  // the partner's key column
+    const uint32_t got = k == 0 ? send : quad_xor(send, k);
+    bits |= got << (4 * (c0 + (t ^ k)));
+  }
+  return bits;
+}
 template <int NC>
 __device__ __forceinline__ uint32_t dropout_col_bits(const Dropout& d, int j, int q4, uint32_t bh) {
   static_assert(NC % 4 == 0 && NC <= 8, "query quads come in groups of four, 32 bits at most");
-  const int t = j & 3;
   uint32_t bits = 0;
 #pragma unroll
   for (int c0 = 0; c0 < NC; c0 += 4) {
-    const u32x4 w = philox4x32_10((uint32_t)(q4 + 8 * (c0 + t)) >> 2, (uint32_t)j >> 2, bh, d.offset, d.k0, d.k1);
-    uint32_t kb = 0;  // bit 4 b + r: key byte b of query row r kept
+    Philox g = dropout_col_state(d, j, q4, bh, c0);
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int b = 0; b < 4; ++b) kb |= (((w[r] >> (8 * b)) & 0xFFu) >= d.p8 ? 1u : 0u) << (4 * b + r);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint32_t send = (kb >> (4 * (t ^ k))) & 0xFu;  // the partner's key column
-      const uint32_t got = k == 0 ? send : quad_xor(send, k);
-      bits |= got << (4 * (c0 + (t ^ k)));
-    }
+    for (int r = 0; r < 10; ++r) g.round(r);
+    bits |= dropout_col_bits_of(d, j, g, c0);
   }
   return bits;
 }
