@@ -567,6 +567,9 @@ void bwd_dkdv_kernel(BwdKParams p) {
 #ifndef FA_BWD_TILE_K_D128
 #define FA_BWD_TILE_K_D128 64
 #endif
+#ifndef FA_BWD_TILE_K_DROP_D128
+#define FA_BWD_TILE_K_DROP_D128 64
+#endif
 // FA_BWD_DQ_PIPE: the dQ tile as one stream of MFMAs with the P and dS work in slices
 // between them (1), or as separate product and element phases (0).
 #ifndef FA_BWD_DQ_PIPE
@@ -597,7 +600,7 @@ void bwd_dq_kernel(BwdKParams p) {
   constexpr int NDB = D / 32;
   constexpr int NKK = D / 16;
   constexpr int TILE = BC * D;
-  constexpr bool PIPE = FA_BWD_DQ_PIPE && !DROP && NKB == 2;
+  constexpr bool PIPE = FA_BWD_DQ_PIPE && NKB == 2;
 
   // Double buffers: one array [K0 | V0 | K1 | V1] for the pipelined tile (inline-assembly
   // reads, the buffer named by the immediate offset); separate arrays named statically
@@ -755,6 +758,8 @@ void bwd_dq_kernel(BwdKParams p) {
         e1 = (k >= 0 && k < len) ? ((k + 1) * 16) / len : 0;
       };
       bf16x8 dsb[2 * NKB];
+      uint32_t dw[4 * NKB];  // dropout keep words (see the S slices)
+      Philox rng{};
 #pragma unroll
       for (int m = 0; m < AH; ++m) fetch(m);
       static_for<NM>([&](auto mc) __attribute__((always_inline)) {
@@ -763,8 +768,20 @@ void bwd_dq_kernel(BwdKParams p) {
         lds_wait(nrd - 1 - ia[m % (AH + 1)]);
         __builtin_amdgcn_sched_barrier(0);
         const bf16x8 a = ra[m % (AH + 1)];
-        if (m < NS)
+        if (m < NS) {
           sacc[m / NKK] = mfma_bf16(a, qf[m % NKK], sacc[m / NKK]);
+          if constexpr (DROP) {
+            // Keep words of key block m / NKK (key quads 4 kb .. 4 kb + 3 of this lane's
+            // query): that call's ten rounds run between the block's S products.
+            const int kb = m / NKK, k = m % NKK;
+#pragma unroll
+            for (int r = (k * 10) / NKK; r < ((k + 1) * 10) / NKK; ++r) {
+              if (r == 0) rng = dropout_row_state(p.drop, qrow, kv0 + 4 * g, (uint32_t)inst, 4 * kb);
+              rng.round(r);
+              if (r == 9) dropout_row_words_of<4 * NKB>(qrow, rng, 4 * kb, dw);
+            }
+          }
+        }
         else if (m < 2 * NS)
           dpacc[(m - NS) / NKK] = mfma_bf16(a, df[(m - NS) % NKK], dpacc[(m - NS) / NKK]);
         else
@@ -792,7 +809,14 @@ void bwd_dq_kernel(BwdKParams p) {
           share(m, w0, len, e0, e1);
 #pragma unroll
           for (int e = e0; e < e1; ++e) {
-            dpacc[kb][e] = sacc[kb][e] * (dpacc[kb][e] - d_q);
+            if constexpr (DROP) {
+              // dS = P (dP o Z / (1 - p) - D); register e of block kb is byte e % 4 of word e / 4
+              const uint32_t w = dw[4 * kb + e / 4];
+              const float z = ((w >> (8 * (e % 4))) & 0xFFu) >= p.drop.p8 ? p.drop.scale : 0.f;
+              dpacc[kb][e] = sacc[kb][e] * fmaf(dpacc[kb][e], z, -d_q);
+            } else {
+              dpacc[kb][e] = sacc[kb][e] * (dpacc[kb][e] - d_q);
+            }
             if ((e & 7) == 7) {
               const int h = e - 7;
               const f32x16& S = dpacc[kb];
@@ -950,8 +974,7 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s) {
 
   timer_begin("fa_bwd_dq", s);
   if (a.d == 128) {
-    // (32-key tiles with dropout: the generator's registers do not fit next to 64-key tiles.)
-    if (drop) bwd_dq_kernel<128, 32, false, false, true><<<grid, block, 0, s>>>(p);
+    if (drop) bwd_dq_kernel<128, FA_BWD_TILE_K_DROP_D128, false, false, true><<<grid, block, 0, s>>>(p);
     else if (sparse && smask) bwd_dq_kernel<128, TK128, true, true><<<grid, block, 0, s>>>(p);
     else if (sparse) bwd_dq_kernel<128, TK128, true><<<grid, block, 0, s>>>(p);
     else bwd_dq_kernel<128, TK128, false><<<grid, block, 0, s>>>(p);

@@ -417,6 +417,29 @@ __device__ __forceinline__ uint32_t quad_xor(uint32_t v, int k) {
                           : (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x1B, 0xF, 0xF, false));  // [3,2,1,0]
 }
 
+// The generator state of this lane's call for key quads c0 .. c0 + 3 (see below).
+__device__ __forceinline__ Philox dropout_row_state(const Dropout& d, int i, int key0, uint32_t bh, int c0) {
+  const int t = i & 3;
+  return Philox{(uint32_t)i >> 2, (uint32_t)(key0 + 8 * (c0 + t)) >> 2, bh, d.offset, d.k0, d.k1};
+}
+// Words c0 .. c0 + 3 of the keep words below from that call's output.
+template <int NC>
+__device__ __forceinline__ void dropout_row_words_of(int i, const Philox& w, int c0, uint32_t (&out)[NC]) {
+  const int t = i & 3;
+  const uint32_t wr[4] = {w.c0, w.c1, w.c2, w.c3};
+  uint32_t got[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int want = t ^ k;  // the word the partner lane (t ^ k) needs
+    const uint32_t send = want == 0 ? wr[0] : (want == 1 ? wr[1] : (want == 2 ? wr[2] : wr[3]));
+    got[k] = k == 0 ? send : quad_xor(send, k);  // my word of quad c0 + (t ^ k)
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int k = j ^ t;
+    out[c0 + j] = k == 0 ? got[0] : (k == 1 ? got[1] : (k == 2 ? got[2] : got[3]));
+  }
+}
 // Keep words of NC key quads (keys key0 + 8 c .. + 3) for this lane's query i,
 // where the four lanes of each lane quad hold queries 4 m .. 4 m + 3 (i mod 4 =
 // lane mod 4). The four lanes need the same generator calls (one word each), so
@@ -426,22 +449,12 @@ template <int NC>
 __device__ __forceinline__ void dropout_row_words(const Dropout& d, int i, int key0, uint32_t bh,
                                                   uint32_t (&out)[NC]) {
   static_assert(NC % 4 == 0, "key quads come in groups of four");
-  const int t = i & 3;
 #pragma unroll
   for (int c0 = 0; c0 < NC; c0 += 4) {
-    const u32x4 w = philox4x32_10((uint32_t)i >> 2, (uint32_t)(key0 + 8 * (c0 + t)) >> 2, bh, d.offset, d.k0, d.k1);
-    uint32_t got[4];
+    Philox g = dropout_row_state(d, i, key0, bh, c0);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int want = t ^ k;  // the word the partner lane (t ^ k) needs
-      const uint32_t send = want == 0 ? w[0] : (want == 1 ? w[1] : (want == 2 ? w[2] : w[3]));
-      got[k] = k == 0 ? send : quad_xor(send, k);  // my word of quad c0 + (t ^ k)
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int k = j ^ t;
-      out[c0 + j] = k == 0 ? got[0] : (k == 1 ? got[1] : (k == 2 ? got[2] : got[3]));
-    }
+    for (int r = 0; r < 10; ++r) g.round(r);
+    dropout_row_words_of<NC>(i, g, c0, out);
   }
 }
 
