@@ -133,7 +133,7 @@ void bwd_dkdv_kernel(BwdKParams p) {
   constexpr int NKK = D / 16;
   constexpr int TILE = BRQ * D;
   static_assert(BRQ <= 64, "row statistics use one 64-lane copy");
-  constexpr bool PIPE = FA_BWD_DKDV_PIPE;
+  constexpr bool PIPE = FA_BWD_DKDV_PIPE && (!VLDS || NQB == 1);  // (one V row read per dP product)
 
   // Double buffers. The pipelined tile reads them only through inline assembly, so
   // they share one array [Q0 | dO0 | Q1 | dO1]: each lane's read addresses are then
