@@ -9,13 +9,14 @@
 // O = P V: with D_i = rowsum(dO o O)_i,
 //   dV = P^T dO,  dP = dO V^T,  dS = P o (dP - D),  dQ = scale dS K,  dK = scale dS^T Q.
 //
-// Kernels (same stream):
-//   bwd_prep:  D and LSE log2(e) per row.
+// Kernels (same stream, in this order):
+//   bwd_dq:    one workgroup per (instance, 128-query block), 4 waves x 32 queries;
+//              it first forms D and LSE log2(e) for its rows (kept in registers and
+//              written to the workspace), then keeps dQ in registers while it
+//              streams the key tiles its rows see.
 //   bwd_dkdv:  one workgroup per (instance, 128-key block), 4 waves x 32 keys; dK
 //              and dV of its keys stay in registers while it streams the query
-//              tiles that may see them.
-//   bwd_dq:    one workgroup per (instance, 128-query block), 4 waves x 32 queries;
-//              dQ stays in registers while it streams the key tiles its rows see.
+//              tiles that may see them, reading D and LSE log2(e) per tile.
 // dQ is computed in its own pass (recomputing S and dP there) rather than
 // accumulated across key blocks with atomics: each output is written once, by
 // one workgroup, so the result is deterministic and no f32 accumulator is needed.
@@ -56,37 +57,6 @@ constexpr int kBwdBlock = 128;  // keys (dK/dV pass) or queries (dQ pass) per wo
 #ifndef FA_BWD_WAVES_PER_EU
 #define FA_BWD_WAVES_PER_EU 2
 #endif
-
-// ------------------------------------------------------------------------------ prep
-
-// One row per D/8 threads: D = sum_i dO_i O_i (f32); lse2 = LSE log2(e), or +inf
-// when the row has no key so that recomputed probabilities are 0.
-template <int D>
-__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdKParams p) {
-  constexpr int TPR = D / 8;
-  const int tid = threadIdx.x;
-  const int64_t row = (int64_t)blockIdx.x * (256 / TPR) + tid / TPR;
-  const int sub = tid % TPR;
-  const int64_t total = (int64_t)p.B * p.H * p.N;
-  float acc = 0.f;
-  if (row < total) {
-    const int64_t inst = row / p.N;
-    const int n = (int)(row - inst * p.N);
-    const int b = (int)(inst / p.H), h = (int)(inst - (int64_t)b * p.H);
-    const int64_t off = (int64_t)b * p.sb + (int64_t)h * p.sh + (int64_t)n * p.sn + 8 * sub;
-    const bf16x8 ov = *reinterpret_cast<const bf16x8*>(p.o + off);
-    const bf16x8 dv = *reinterpret_cast<const bf16x8*>(p.dout + off);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc = fmaf((float)ov[i], (float)dv[i], acc);
-  }
-#pragma unroll
-  for (int off = TPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
-  if (row < total && sub == 0) {
-    p.delta[row] = acc;
-    const float l = p.lse[row];
-    p.lse2[row] = (l == kNegInf) ? kPosInf : l * kLog2e;
-  }
-}
 
 // ------------------------------------------------------------------------------ dK, dV
 
@@ -663,8 +633,24 @@ void bwd_dq_kernel(BwdKParams p) {
     qf[kk] = *reinterpret_cast<const bf16x8*>(Qh + qoff + 16 * kk);
     df[kk] = *reinterpret_cast<const bf16x8*>(dOh + qoff + 16 * kk);
   }
-  const float lse2_q = p.lse2[rowbase + qc];
-  const float d_q = p.delta[rowbase + qc];
+  // The row statistics the recomputation needs: D = sum_i dO_i O_i (this lane's
+  // half of the dims, then its partner lane's) and lse2 = LSE log2(e), or +inf
+  // when the row has no key so that recomputed probabilities are 0. The dK/dV
+  // pass, launched after this one, reads them from the workspace.
+  float d_half = 0.f;
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) {
+    const bf16x8 ov = *reinterpret_cast<const bf16x8*>(p.o + base + qoff + 16 * kk);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) d_half = fmaf((float)ov[i], (float)df[kk][i], d_half);
+  }
+  const float d_q = pair_sum(d_half);
+  const float lse_q = p.lse[rowbase + qc];
+  const float lse2_q = (lse_q == kNegInf) ? kPosInf : lse_q * kLog2e;
+  if (qrow < N && g == 0) {
+    p.delta[rowbase + qrow] = d_q;
+    p.lse2[rowbase + qrow] = lse2_q;
+  }
 
   f32x16 dqacc[NDB];
 #pragma unroll
@@ -941,37 +927,13 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s) {
   const bool smask = a.causal || a.key_len != nullptr;
   const bool drop = a.dropout.p8 != 0 && !sparse;
   p.drop = a.dropout;
-  const int64_t rows = (int64_t)a.B * a.H * a.N;
   const dim3 block(256);
-
-  const int rows_per_wg = 256 / (a.d / 8);
-  const dim3 grid_prep((unsigned)((rows + rows_per_wg - 1) / rows_per_wg));
-  timer_begin("fa_bwd_prep", s);
-  if (a.d == 128) bwd_prep_kernel<128><<<grid_prep, block, 0, s>>>(p);
-  else bwd_prep_kernel<64><<<grid_prep, block, 0, s>>>(p);
-  timer_end(s);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
 
   constexpr int TQ128 = FA_BWD_TILE_Q_D128, TQ64 = FA_BWD_TILE_Q_D64;
   constexpr int TK128 = FA_BWD_TILE_K_D128, TK64 = FA_BWD_TILE_K_D64;
   const dim3 grid((unsigned)(a.B * a.H * p.n_blocks));
-  timer_begin("fa_bwd_dkdv", s);
-  if (a.d == 128) {
-    if (drop) bwd_dkdv_kernel<128, TQ128, false, true, false, true><<<grid, block, 0, s>>>(p);
-    else if (sparse && smask) bwd_dkdv_kernel<128, TQ128, true, true, true><<<grid, block, 0, s>>>(p);
-    else if (sparse) bwd_dkdv_kernel<128, TQ128, true, true><<<grid, block, 0, s>>>(p);
-    else bwd_dkdv_kernel<128, TQ128, false, true><<<grid, block, 0, s>>>(p);
-  } else {
-    if (drop) bwd_dkdv_kernel<64, TQ64, false, false, false, true><<<grid, block, 0, s>>>(p);
-    else if (sparse && smask) bwd_dkdv_kernel<64, TQ64, true, false, true><<<grid, block, 0, s>>>(p);
-    else if (sparse) bwd_dkdv_kernel<64, TQ64, true, false><<<grid, block, 0, s>>>(p);
-    else bwd_dkdv_kernel<64, TQ64, false, false><<<grid, block, 0, s>>>(p);
-  }
-  timer_end(s);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-
+  // The dQ pass first: it also writes each row's D and lse2, which the dK/dV
+  // pass reads for every query tile it visits.
   timer_begin("fa_bwd_dq", s);
   if (a.d == 128) {
     if (drop) bwd_dq_kernel<128, FA_BWD_TILE_K_DROP_D128, false, false, true><<<grid, block, 0, s>>>(p);
@@ -983,6 +945,22 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s) {
     else if (sparse && smask) bwd_dq_kernel<64, TK64, true, true><<<grid, block, 0, s>>>(p);
     else if (sparse) bwd_dq_kernel<64, TK64, true><<<grid, block, 0, s>>>(p);
     else bwd_dq_kernel<64, TK64, false><<<grid, block, 0, s>>>(p);
+  }
+  timer_end(s);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  timer_begin("fa_bwd_dkdv", s);
+  if (a.d == 128) {
+    if (drop) bwd_dkdv_kernel<128, TQ128, false, true, false, true><<<grid, block, 0, s>>>(p);
+    else if (sparse && smask) bwd_dkdv_kernel<128, TQ128, true, true, true><<<grid, block, 0, s>>>(p);
+    else if (sparse) bwd_dkdv_kernel<128, TQ128, true, true><<<grid, block, 0, s>>>(p);
+    else bwd_dkdv_kernel<128, TQ128, false, true><<<grid, block, 0, s>>>(p);
+  } else {
+    if (drop) bwd_dkdv_kernel<64, TQ64, false, false, false, true><<<grid, block, 0, s>>>(p);
+    else if (sparse && smask) bwd_dkdv_kernel<64, TQ64, true, false, true><<<grid, block, 0, s>>>(p);
+    else if (sparse) bwd_dkdv_kernel<64, TQ64, true, false><<<grid, block, 0, s>>>(p);
+    else bwd_dkdv_kernel<64, TQ64, false, false><<<grid, block, 0, s>>>(p);
   }
   timer_end(s);
   return hipGetLastError();
