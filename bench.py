@@ -60,6 +60,22 @@ def kept_pairs(case) -> int:
     return total * H
 
 
+def device_peak_bf16_tflops():
+    """Dense bf16 MFMA peak implied by the device's own report: peak engine clock x CUs x 4096
+    flop per clock per CU (None if the runtime does not report it)."""
+    import ctypes
+    import torch
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        khz = ctypes.c_int(0)
+        if hip.hipDeviceGetAttribute(ctypes.byref(khz), 5, 0) != 0:  # hipDeviceAttributeClockRate (kHz)
+            return None
+        cus = torch.cuda.get_device_properties(0).multi_processor_count
+        return round(khz.value * 1e3 * cus * 4096 / 1e12, 1)
+    except OSError:
+        return None
+
+
 def sources_hash() -> str:
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
@@ -414,6 +430,8 @@ def main():
         "kernels": {k: {"mean_ms": round(v["mean_ms"], 4), "launches": v["launches"],
                         "share": round(v["share"], 4)} for k, v in kt.items()},
         "roofline": roofline,
+        "device_peak_bf16": {"value": device_peak_bf16_tflops(), "unit": "TFLOP/s",
+                             "note": "reported peak engine clock x CUs x 4096 flop/clk/CU"},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)
