@@ -100,7 +100,7 @@ def traffic_for(kernel: str, workload: str):
 
 # Library timer names of the kernels, by a fragment of their symbol.
 KERNEL_NAMES = {"fwd_bf16_kernel": "fa_fwd_bf16", "fwd_f32_kernel": "fa_fwd_f32",
-                "bwd_dkdv_kernel": "fa_bwd_dkdv", "bwd_dq_kernel": "fa_bwd_dq", "block_lists_kernel": "fa_block_lists"}
+                "bwd_dkdv_kernel": "fa_bwd_dkdv", "bwd_dq_kernel": "fa_bwd_dq"}
 
 
 def calibrate_copy(nbytes: int = 1 << 30, launches: int = 3):
@@ -376,7 +376,7 @@ def main():
     with fa.KernelTimer() as timer:  # the same K steps again, each launch bracketed by events
         timed_ms = timed_steps()
         kt = {}
-        for name in ("fa_fwd_bf16", "fa_bwd_dq", "fa_bwd_dkdv", "fa_block_lists"):
+        for name in ("fa_fwd_bf16", "fa_bwd_dq", "fa_bwd_dkdv"):
             ms, n = timer.read(name)
             if n:
                 kt[name] = {"mean_ms": ms / n, "launches": n, "share": ms / timed_ms}

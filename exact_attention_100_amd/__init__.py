@@ -184,11 +184,11 @@ def blocksparse_fwd(q, k, v, block_mask, block_size, scale=None, causal=False, k
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
     _lse_check(lse, q)
     need = int(lib().fa_blocksparse_workspace_bytes(ctypes.byref(d), int(block_size), 0))
-    ws = _workspace(need, q, workspace)
+    ws = None if (need == 0 and workspace is None) else _workspace(need, q, workspace)
     st = lib().fa_blocksparse_fwd(ctypes.byref(d), q.data_ptr(), k.data_ptr(), v.data_ptr(),
                                   _scale(scale, q.shape[-1]), int(bool(causal)), _ptr(kl),
                                   block_mask.data_ptr(), int(block_size), o.data_ptr(), lse.data_ptr(),
-                                  ws.data_ptr(), ws.numel() * ws.element_size(), _stream(q))
+                                  _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(q))
     _check(st, "fa_blocksparse_fwd")
     return o, lse
 

@@ -136,29 +136,10 @@ size_t bwd_ws_bytes(const fa_desc* d) {
   return 2 * round_up(rows * sizeof(float));
 }
 
-size_t lists_bytes(int nb) { return 2 * round_up((size_t)(nb + 1) * 4) + 2 * round_up((size_t)nb * nb * 4); }
-
 int check_block(const fa_desc* d, int32_t bs) {
   if (bs < 128 || bs % 128 != 0 || d->N % bs != 0) return FA_ERR_INVALID;
   if (d->N / bs > 1024) return FA_ERR_UNSUPPORTED;
   return FA_OK;
-}
-
-struct Lists {
-  int32_t *row_ptr, *col_idx, *col_ptr, *row_idx;
-};
-
-Lists carve_lists(void* ws, int nb) {
-  char* p = static_cast<char*>(ws);
-  Lists l;
-  l.row_ptr = reinterpret_cast<int32_t*>(p);
-  p += round_up((size_t)(nb + 1) * 4);
-  l.col_ptr = reinterpret_cast<int32_t*>(p);
-  p += round_up((size_t)(nb + 1) * 4);
-  l.col_idx = reinterpret_cast<int32_t*>(p);
-  p += round_up((size_t)nb * nb * 4);
-  l.row_idx = reinterpret_cast<int32_t*>(p);
-  return l;
 }
 
 void carve_bwd(const fa_desc* d, void* ws, BwdArgs& a) {
@@ -312,14 +293,15 @@ extern "C" int fa_bwd_dropout(const fa_desc* desc, const void* Q, const void* K,
 
 extern "C" size_t fa_blocksparse_workspace_bytes(const fa_desc* desc, int32_t block_size, int backward) {
   if (check_desc(desc) || check_block(desc, block_size)) return 0;
-  const size_t lists = lists_bytes(desc->N / block_size);
-  return backward ? lists + bwd_ws_bytes(desc) : lists;
+  return backward ? bwd_ws_bytes(desc) : 0;
 }
 
 extern "C" int fa_blocksparse_fwd(const fa_desc* desc, const void* Q, const void* K, const void* V,
                                   float scale, int causal, const int32_t* key_len,
                                   const uint8_t* block_mask, int32_t block_size, void* O, float* LSE,
                                   void* workspace, size_t workspace_bytes, void* stream) {
+  (void)workspace;  // the forward needs none (each workgroup reads its row of the block mask)
+  (void)workspace_bytes;
   int st = check_desc(desc);
   if (st) return st;
   if (desc->dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
@@ -327,17 +309,11 @@ extern "C" int fa_blocksparse_fwd(const fa_desc* desc, const void* Q, const void
   if ((st = check_ptrs({Q, K, V, O, LSE}))) return st;
   if (!block_mask) return FA_ERR_INVALID;
   if ((st = check_block(desc, block_size))) return st;
-  const int nb = desc->N / block_size;
-  if (!workspace || !aligned16(workspace) || workspace_bytes < lists_bytes(nb)) return FA_ERR_WORKSPACE;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const Lists l = carve_lists(workspace, nb);
-  hipError_t e = launch_block_lists(block_mask, nb, causal != 0, l.row_ptr, l.col_idx, l.col_ptr, l.row_idx, s);
-  if (e != hipSuccess) return FA_ERR_HIP;
   FwdArgs a = fwd_args(desc, Q, K, V, scale, causal != 0, key_len, O, LSE);
-  a.row_ptr = l.row_ptr;
-  a.col_idx = l.col_idx;
+  a.block_mask = block_mask;
+  a.nb = desc->N / block_size;
   a.block_size = block_size;
-  return hip_status(launch_fwd_bf16(a, s));
+  return hip_status(launch_fwd_bf16(a, static_cast<hipStream_t>(stream)));
 }
 
 extern "C" int fa_blocksparse_bwd(const fa_desc* desc, const void* Q, const void* K, const void* V,
@@ -352,19 +328,11 @@ extern "C" int fa_blocksparse_bwd(const fa_desc* desc, const void* Q, const void
   if ((st = check_ptrs({Q, K, V, O, dO, LSE, dQ, dK, dV}))) return st;
   if (!block_mask) return FA_ERR_INVALID;
   if ((st = check_block(desc, block_size))) return st;
-  const int nb = desc->N / block_size;
-  const size_t lb = lists_bytes(nb);
-  if (!workspace || !aligned16(workspace) || workspace_bytes < lb + bwd_ws_bytes(desc)) return FA_ERR_WORKSPACE;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const Lists l = carve_lists(workspace, nb);
-  hipError_t e = launch_block_lists(block_mask, nb, causal != 0, l.row_ptr, l.col_idx, l.col_ptr, l.row_idx, s);
-  if (e != hipSuccess) return FA_ERR_HIP;
+  if (!workspace || !aligned16(workspace) || workspace_bytes < bwd_ws_bytes(desc)) return FA_ERR_WORKSPACE;
   BwdArgs a = bwd_args(desc, Q, K, V, O, dO, LSE, scale, causal != 0, key_len, dQ, dK, dV);
-  carve_bwd(desc, static_cast<char*>(workspace) + lb, a);
-  a.row_ptr = l.row_ptr;
-  a.col_idx = l.col_idx;
-  a.col_ptr = l.col_ptr;
-  a.row_idx = l.row_idx;
+  carve_bwd(desc, workspace, a);
+  a.block_mask = block_mask;
+  a.nb = desc->N / block_size;
   a.block_size = block_size;
-  return hip_status(launch_bwd_bf16(a, s));
+  return hip_status(launch_bwd_bf16(a, static_cast<hipStream_t>(stream)));
 }

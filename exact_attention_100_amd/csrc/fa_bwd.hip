@@ -43,10 +43,8 @@ struct BwdKParams {
   float scale;
   int causal;
   const int32_t* key_len;
-  const int32_t* row_ptr;  // block-sparse: kept key blocks per query block
-  const int32_t* col_idx;
-  const int32_t* col_ptr;  // block-sparse: kept query blocks per key block
-  const int32_t* row_idx;
+  const uint8_t* bmask;    // block-sparse: uint8 [nb][nb], row = query block
+  int nb;
   int bs;
   int n_blocks;            // 128-row blocks of N
   Dropout drop;            // p8 == 0: none
@@ -125,6 +123,9 @@ void bwd_dkdv_kernel(BwdKParams p) {
   __shared__ __attribute__((aligned(16))) float sDl0[64];
   __shared__ __attribute__((aligned(16))) float sDl1[64];
   __shared__ __attribute__((aligned(16))) bf16 sV[VLDS ? kBwdBlock * D : 8];
+  // Block-sparse: the query blocks that see this key block.
+  __shared__ int16_t sBlk[SPARSE ? kMaxBlocks : 1];
+  __shared__ int sBlkN;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5;
@@ -148,13 +149,13 @@ void bwd_dkdv_kernel(BwdKParams p) {
 
   // The query tiles this key block visits (none when all its keys are past
   // kv_len: dK = dV = 0).
-  int n_qt, qt_begin = 0, cbeg = 0;
+  int n_blk = 0;
+  if constexpr (SPARSE) n_blk = kept_block_list<false>(p.bmask, p.nb, k0 / p.bs, p.causal, sBlk, &sBlkN);
+  int n_qt, qt_begin = 0;
   if (k0 >= kv_len) {
     n_qt = 0;
   } else if (SPARSE) {
-    const int kbs = k0 / p.bs;
-    cbeg = p.col_ptr[kbs];
-    n_qt = (p.col_ptr[kbs + 1] - cbeg) * (p.bs / BRQ);
+    n_qt = n_blk * (p.bs / BRQ);
   } else {
     qt_begin = p.causal ? k0 / BRQ : 0;
     n_qt = (N + BRQ - 1) / BRQ - qt_begin;
@@ -162,7 +163,7 @@ void bwd_dkdv_kernel(BwdKParams p) {
   auto tile_q0 = [&](int t) -> int {
     if (SPARSE) {
       const int tpb = p.bs / BRQ;
-      return p.row_idx[cbeg + t / tpb] * p.bs + (t - (t / tpb) * tpb) * BRQ;
+      return sBlk[t / tpb] * p.bs + (t - (t / tpb) * tpb) * BRQ;
     }
     return (qt_begin + t) * BRQ;
   };
@@ -585,6 +586,9 @@ void bwd_dq_kernel(BwdKParams p) {
   bf16* const bV0 = PIPE ? sT + TILE : sV0;
   bf16* const bK1 = PIPE ? sT + 2 * TILE : sK1;
   bf16* const bV1 = PIPE ? sT + 3 * TILE : sV1;
+  // Block-sparse: this query block's kept key blocks.
+  __shared__ int16_t sBlk[SPARSE ? kMaxBlocks : 1];
+  __shared__ int sBlkN;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5;
@@ -604,12 +608,10 @@ void bwd_dq_kernel(BwdKParams p) {
   const int64_t rowbase = (int64_t)inst * N;
 
   // The key tiles this query block visits (as in the forward).
-  int kv_len = N, n_tiles, blk_begin = 0;
+  int kv_len = N, n_tiles;
   if (p.key_len) kv_len = min(max(p.key_len[b], 0), N);
-  if (SPARSE) {
-    const int rb = q0 / p.bs;
-    blk_begin = p.row_ptr[rb];
-    n_tiles = (p.row_ptr[rb + 1] - blk_begin) * (p.bs / BC);
+  if constexpr (SPARSE) {
+    n_tiles = kept_block_list<true>(p.bmask, p.nb, q0 / p.bs, p.causal, sBlk, &sBlkN) * (p.bs / BC);
   } else {
     int kv_end = kv_len;
     if (p.causal) kv_end = min(kv_end, q0 + kBwdBlock);
@@ -619,7 +621,7 @@ void bwd_dq_kernel(BwdKParams p) {
     if (SPARSE) {
       if (t >= n_tiles) return 0;
       const int tpb = p.bs / BC;
-      return p.col_idx[blk_begin + t / tpb] * p.bs + (t - (t / tpb) * tpb) * BC;
+      return sBlk[t / tpb] * p.bs + (t - (t / tpb) * tpb) * BC;
     }
     return t * BC;
   };
@@ -917,13 +919,11 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s) {
   p.c = fmaxf(a.scale * kLog2e, 1.17549435e-38f);
   p.causal = a.causal;
   p.key_len = a.key_len;
-  p.row_ptr = a.row_ptr;
-  p.col_idx = a.col_idx;
-  p.col_ptr = a.col_ptr;
-  p.row_idx = a.row_idx;
+  p.bmask = a.block_mask;
+  p.nb = a.nb;
   p.bs = a.block_size;
   p.n_blocks = (a.N + kBwdBlock - 1) / kBwdBlock;
-  const bool sparse = a.col_ptr != nullptr;
+  const bool sparse = a.block_mask != nullptr;
   const bool smask = a.causal || a.key_len != nullptr;
   const bool drop = a.dropout.p8 != 0 && !sparse;
   p.drop = a.dropout;
@@ -962,154 +962,6 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s) {
     else if (sparse) bwd_dkdv_kernel<64, TQ64, true, false><<<grid, block, 0, s>>>(p);
     else bwd_dkdv_kernel<64, TQ64, false, false><<<grid, block, 0, s>>>(p);
   }
-  timer_end(s);
-  return hipGetLastError();
-}
-
-// ------------------------------------------------------------------------------ block lists
-
-// One workgroup: per-row (CSR) and per-column (CSC) lists of the kept blocks of
-// an nb x nb mask (nb <= 1024), indices in increasing order. With causal,
-// blocks above the diagonal (key block > query block) are dropped: every
-// element of them is masked. STAGED: the mask (nb * nb <= kStagedMask bytes)
-// is first copied into LDS, so the scans below read LDS instead of making
-// long chains of dependent global loads.
-constexpr int kStagedMask = 65536;
-
-// Exclusive prefix sum of v over the 1024 threads of the workgroup (thread i
-// holds element i); returns element i's prefix, and the total in *total.
-__device__ __forceinline__ int block_exclusive_scan(int v, int32_t* wsum, int* total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
-  if (lane == 63) wsum[wave] = x;
-  __syncthreads();
-  int before = 0, all = 0;
-  for (int w = 0; w < 16; ++w) {
-    const int s = wsum[w];
-    before += w < wave ? s : 0;
-    all += s;
-  }
-  __syncthreads();
-  *total = all;
-  return before + x - v;
-}
-
-template <bool STAGED>
-__global__ __launch_bounds__(1024) void block_lists_kernel(const uint8_t* mask, int nb, int causal,
-                                                           int32_t* row_ptr, int32_t* col_idx,
-                                                           int32_t* col_ptr, int32_t* row_idx) {
-  __shared__ int32_t rcount[1024], ccount[1024], rstart[1024], cstart[1024], wsum[16];
-  __shared__ int32_t cpart[1024];  // per (row slice, column) counts, then their offsets
-  __shared__ __attribute__((aligned(16))) uint8_t smask[STAGED ? kStagedMask : 4];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;  // 16 waves
-  const int total = nb * nb;
-  if (STAGED && (total & 3) == 0 && ((uintptr_t)mask & 3) == 0) {
-    // Dword copies (at most 16 per thread), all issued before the first store.
-    const int words = total >> 2;
-    const uint32_t* m32 = reinterpret_cast<const uint32_t*>(mask);
-    uint32_t* s32 = reinterpret_cast<uint32_t*>(smask);
-    for (int i0 = 0; i0 < words; i0 += 1024 * 4) {
-      uint32_t v[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) v[u] = m32[min(i0 + u * 1024 + tid, words - 1)];
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (i0 + u * 1024 + tid < words) s32[i0 + u * 1024 + tid] = v[u];
-    }
-    __syncthreads();
-  } else if (STAGED) {
-    for (int i0 = 0; i0 < total; i0 += 1024 * 8) {
-      uint8_t v[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = mask[min(i0 + u * 1024 + tid, total - 1)];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int i = i0 + u * 1024 + tid;
-        if (i < total) smask[i] = v[u];
-      }
-    }
-    __syncthreads();
-  }
-  auto keep = [&](int r, int c) -> bool {
-    const uint8_t m = STAGED ? smask[r * nb + c] : mask[(int64_t)r * nb + c];
-    return m != 0 && (!causal || c <= r);
-  };
-  // Row counts: one wave per row, 64 consecutive columns per step (ballot).
-  // Column counts: thread (slice, c) walks column c over its slice of the rows,
-  // so that a wave reads consecutive bytes per step (reading a column across the
-  // lanes of a wave would put them all on one LDS bank) and every thread works.
-  const int nsl = nb >= 1024 ? 1 : 1024 / nb;        // row slices per column
-  const int rows_sl = (nb + nsl - 1) / nsl;          // rows per slice
-  const int sl = tid / nb, col = tid - sl * nb;      // this thread's (slice, column)
-  const bool has_col = sl < nsl;
-  const int r_lo = min(sl * rows_sl, nb), r_hi = min(r_lo + rows_sl, nb);
-  for (int i = wave; i < nb; i += 16) {
-    int rc = 0;
-    for (int j0 = 0; j0 < nb; j0 += 64) rc += __popcll(__ballot(j0 + lane < nb && keep(i, j0 + lane)));
-    if (lane == 0) rcount[i] = rc;
-  }
-  if (has_col) {
-    int cc = 0;
-    for (int r = r_lo; r < r_hi; ++r) cc += keep(r, col);
-    cpart[tid] = cc;
-  }
-  __syncthreads();
-  // Column totals, and each slice's offset within its column (in place).
-  if (tid < nb) {
-    int acc = 0;
-    for (int s = 0; s < nsl; ++s) {
-      const int c = cpart[s * nb + tid];
-      cpart[s * nb + tid] = acc;
-      acc += c;
-    }
-    ccount[tid] = acc;
-  }
-  __syncthreads();
-  int rtot, ctot;
-  const int rs = block_exclusive_scan(tid < nb ? rcount[tid] : 0, wsum, &rtot);
-  const int cs = block_exclusive_scan(tid < nb ? ccount[tid] : 0, wsum, &ctot);
-  if (tid < nb) {
-    rstart[tid] = rs;
-    cstart[tid] = cs;
-    row_ptr[tid] = rs;
-    col_ptr[tid] = cs;
-  }
-  if (tid == 0) {
-    row_ptr[nb] = rtot;
-    col_ptr[nb] = ctot;
-  }
-  __syncthreads();
-  // The lists, in increasing index order. Columns of a row: one wave per row, a
-  // kept entry's slot being the number of kept entries before it (ballot prefix
-  // count). Rows of a column: one thread per column, as for the counts.
-  for (int i = wave; i < nb; i += 16) {
-    int rb = rstart[i];
-    for (int j0 = 0; j0 < nb; j0 += 64) {
-      const bool kr = j0 + lane < nb && keep(i, j0 + lane);
-      const uint64_t br = __ballot(kr);
-      if (kr) col_idx[rb + __popcll(br & ((1ull << lane) - 1ull))] = j0 + lane;
-      rb += __popcll(br);
-    }
-  }
-  if (has_col) {
-    int cp = cstart[col] + cpart[tid];
-    for (int r = r_lo; r < r_hi; ++r)
-      if (keep(r, col)) row_idx[cp++] = r;
-  }
-}
-
-hipError_t launch_block_lists(const uint8_t* mask, int nb, int causal, int32_t* row_ptr, int32_t* col_idx,
-                              int32_t* col_ptr, int32_t* row_idx, hipStream_t s) {
-  timer_begin("fa_block_lists", s);
-  if (nb * nb <= kStagedMask)
-    block_lists_kernel<true><<<dim3(1), dim3(1024), 0, s>>>(mask, nb, causal, row_ptr, col_idx, col_ptr, row_idx);
-  else
-    block_lists_kernel<false><<<dim3(1), dim3(1024), 0, s>>>(mask, nb, causal, row_ptr, col_idx, col_ptr, row_idx);
   timer_end(s);
   return hipGetLastError();
 }

@@ -540,6 +540,45 @@ __device__ __forceinline__ void vec_dma64(float* lds_vec, const float* g, int i0
 // direct-to-LDS copies) have completed: s_waitcnt vmcnt(0).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Block-sparse attention: the kept blocks along one line of an nb x nb block
+// mask, in increasing order, written to `list` (LDS). ROW: mask[line][j], the
+// key blocks seen by query block `line`; otherwise mask[j][line], the query
+// blocks that see key block `line`. With causal, blocks above the diagonal (key
+// block > query block) are dropped: every entry of them is masked. Wave 0 loads
+// the line (all of its loads issued before the first is used) and forms the list
+// with ballots; after a workgroup barrier every thread gets the count. Every
+// thread of the workgroup must call it. nb <= kMaxBlocks.
+constexpr int kMaxBlocks = 1024;
+template <bool ROW>
+__device__ __forceinline__ int kept_block_list(const uint8_t* mask, int nb, int line, int causal, int16_t* list,
+                                               int* count) {
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    constexpr int K = kMaxBlocks / 64;
+    uint32_t m[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int j = 64 * k + lane;
+      m[k] = 0;
+      if (j < nb) m[k] = ROW ? mask[(int64_t)line * nb + j] : mask[(int64_t)j * nb + line];
+    }
+    int n = 0;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      if (64 * k < nb) {  // uniform
+        const int j = 64 * k + lane;
+        const bool keep = j < nb && m[k] != 0 && (!causal || (ROW ? j <= line : j >= line));
+        const uint64_t bal = __ballot(keep);
+        if (keep) list[n + __popcll(bal & ((1ull << lane) - 1ull))] = (int16_t)j;
+        n += __popcll(bal);
+      }
+    }
+    if (lane == 0) *count = n;
+  }
+  __syncthreads();
+  return *count;
+}
+
 // Workgroup -> (instance, tile) schedule. Consecutive workgroup ids are handed
 // to the 8 XCDs in turn; when the instance count allows it, all tiles of one
 // (batch, head) instance go to the same XCD so its K/V (or Q/dO) re-reads hit

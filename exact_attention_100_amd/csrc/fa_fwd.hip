@@ -37,8 +37,8 @@ struct FwdKParams {
   float c;  // scale * log2(e): scores are kept in the base-2 domain
   int causal;
   const int32_t* key_len;
-  const int32_t* row_ptr;
-  const int32_t* col_idx;
+  const uint8_t* bmask;  // block-sparse: uint8 [nb][nb], row = query block
+  int nb;
   int bs;
   int n_qblocks;
   Dropout drop;
@@ -51,21 +51,21 @@ constexpr float kRescaleSlack = 8.f;
 struct FwdRange {
   int kv_len;    // keys >= kv_len are masked for every row of this instance
   int n_tiles;   // tiles to visit
-  int blk_begin; // sparse: first entry of this query block's list
+  const int16_t* blocks;  // sparse: this query block's kept key blocks (LDS)
 };
 
+// Sparse: `blocks` / `n_blocks` are the query block's kept key blocks (blocks above
+// the diagonal already dropped when causal); key_len and the diagonal blocks mask
+// per element.
 template <int BC, bool SPARSE>
-__device__ __forceinline__ FwdRange fwd_range(const FwdKParams& p, int b, int q0) {
+__device__ __forceinline__ FwdRange fwd_range(const FwdKParams& p, int b, int q0, const int16_t* blocks = nullptr,
+                                              int n_blocks = 0) {
   FwdRange r;
   r.kv_len = p.N;
-  r.blk_begin = 0;
+  r.blocks = blocks;
   if (p.key_len) r.kv_len = min(max(p.key_len[b], 0), p.N);
   if (SPARSE) {
-    // The row's kept blocks (blocks above the diagonal are already dropped from
-    // the lists when causal); key_len and the diagonal blocks mask per element.
-    const int rb = q0 / p.bs;
-    r.blk_begin = p.row_ptr[rb];
-    r.n_tiles = (p.row_ptr[rb + 1] - r.blk_begin) * (p.bs / BC);
+    r.n_tiles = n_blocks * (p.bs / BC);
   } else {
     int kv_end = r.kv_len;
     if (p.causal) kv_end = min(kv_end, q0 + kFwdRows);
@@ -79,7 +79,7 @@ __device__ __forceinline__ int fwd_tile_kv0(const FwdKParams& p, const FwdRange&
   if (SPARSE) {
     if (t >= r.n_tiles) return 0;  // (the prologue of an empty row list)
     const int tpb = p.bs / BC;
-    const int blk = p.col_idx[r.blk_begin + t / tpb];
+    const int blk = r.blocks[t / tpb];
     return blk * p.bs + (t - (t / tpb) * tpb) * BC;
   }
   return t * BC;
@@ -213,6 +213,9 @@ void fwd_bf16_kernel(FwdKParams p) {
   bf16* const sK1 = sT + TILE;
   bf16* const sV0 = sT + 2 * TILE;
   bf16* const sV1 = sT + 3 * TILE;
+  // Block-sparse: this query block's kept key blocks.
+  __shared__ int16_t sBlk[SPARSE ? kMaxBlocks : 1];
+  __shared__ int sBlkN;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5;
@@ -227,7 +230,9 @@ void fwd_bf16_kernel(FwdKParams p) {
   const bf16* Vh = static_cast<const bf16*>(p.v) + base;
   const int q0 = qb * kFwdRows;
   const int qrow = q0 + wave * 32 + l32;
-  const FwdRange rg = fwd_range<BC, SPARSE>(p, b, q0);
+  int n_blk = 0;
+  if constexpr (SPARSE) n_blk = kept_block_list<true>(p.bmask, p.nb, q0 / p.bs, p.causal, sBlk, &sBlkN);
+  const FwdRange rg = fwd_range<BC, SPARSE>(p, b, q0, sBlk, n_blk);
 
   // Every global load is unconditional: rows past the end are clamped to row
   // N - 1, whose values then only ever meet probability 0 (masked keys) or feed
@@ -582,8 +587,8 @@ static FwdKParams make_params(const FwdArgs& a) {
   p.c = fmaxf(a.scale * kLog2e, 1.17549435e-38f);
   p.causal = a.causal;
   p.key_len = a.key_len;
-  p.row_ptr = a.row_ptr;
-  p.col_idx = a.col_idx;
+  p.bmask = a.block_mask;
+  p.nb = a.nb;
   p.bs = a.block_size;
   p.n_qblocks = (a.N + kFwdRows - 1) / kFwdRows;
   p.drop = a.dropout;
@@ -605,7 +610,7 @@ static FwdKParams make_params(const FwdArgs& a) {
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s) {
   const FwdKParams p = make_params(a);
   const dim3 grid((unsigned)(a.B * a.H * p.n_qblocks)), block(256);
-  const bool sparse = a.row_ptr != nullptr;
+  const bool sparse = a.block_mask != nullptr;
   const bool smask = a.causal || a.key_len != nullptr;
   timer_begin("fa_fwd_bf16", s);
   constexpr int BC128 = FA_FWD_BC_D128, BC64 = FA_FWD_BC_D64, BCS64 = FA_FWD_BC_SPARSE_D64;

@@ -20,9 +20,9 @@ struct FwdArgs {
   float scale;
   int causal;
   const int32_t* key_len;  // device [B] or nullptr
-  // Block-sparse (row_ptr != nullptr): CSR lists of kept key blocks per query block.
-  const int32_t* row_ptr;
-  const int32_t* col_idx;
+  // Block-sparse (block_mask != nullptr): device uint8 [nb][nb], row = query block.
+  const uint8_t* block_mask;
+  int nb;
   int block_size;
   Dropout dropout;  // p8 == 0: none
 };
@@ -45,12 +45,9 @@ struct BwdArgs {
   // workspace sections
   float* delta;   // [B, H, N]: rowsum(dO o O)
   float* lse2;    // [B, H, N]: LSE * log2(e) (+inf for rows with no key)
-  // Block-sparse (col_ptr != nullptr): CSR lists of kept key blocks per query
-  // block and CSC lists of kept query blocks per key block.
-  const int32_t* row_ptr;
-  const int32_t* col_idx;
-  const int32_t* col_ptr;
-  const int32_t* row_idx;
+  // Block-sparse (block_mask != nullptr): device uint8 [nb][nb], row = query block.
+  const uint8_t* block_mask;
+  int nb;
   int block_size;
   Dropout dropout;  // p8 == 0: none
 };
@@ -62,9 +59,5 @@ void timer_end(hipStream_t stream);
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s);
-// Builds row_ptr[nb+1], col_idx[nb*nb], col_ptr[nb+1], row_idx[nb*nb] from the mask
-// (blocks above the diagonal dropped when causal).
-hipError_t launch_block_lists(const uint8_t* mask, int nb, int causal, int32_t* row_ptr, int32_t* col_idx,
-                              int32_t* col_ptr, int32_t* row_idx, hipStream_t s);
 
 }  // namespace fa

@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define FA_VERSION 102
+#define FA_VERSION 103
 
 enum fa_status {
   FA_OK = 0,
@@ -98,9 +98,10 @@ int fa_bwd(const fa_desc* desc, const void* Q, const void* K, const void* V, con
            const void* dO, const float* LSE, float scale, int causal, const int32_t* key_len,
            void* dQ, void* dK, void* dV, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Bytes of device workspace the block-sparse calls need for block_size `bs`
- * (the per-row and per-column lists of kept blocks; the backward adds the
- * fa_bwd workspace). Returns 0 for an invalid descriptor or block size. */
+/* Bytes of device workspace the block-sparse calls need for block_size `bs`:
+ * none for the forward (each workgroup reads its own row of the block mask),
+ * the fa_bwd workspace for the backward. Returns 0 for an invalid descriptor or
+ * block size. */
 size_t fa_blocksparse_workspace_bytes(const fa_desc* desc, int32_t block_size, int backward);
 
 /* Block-sparse forward: fa_fwd restricted to the nonzero blocks of
@@ -110,7 +111,9 @@ size_t fa_blocksparse_workspace_bytes(const fa_desc* desc, int32_t block_size, i
  * fa_fwd, may be 0 / NULL) combine with the block mask by AND: an entry is kept
  * iff its block is nonzero, and it is causal-allowed, and its key is below the
  * batch's key length. Blocks above the diagonal are then skipped when causal.
- * Requires N % bs == 0 and bs a positive multiple of 128. bf16 only. */
+ * Requires N % bs == 0, bs a positive multiple of 128 and N / bs <= 1024
+ * (else FA_ERR_UNSUPPORTED). bf16 only. `workspace` is not used (it may be
+ * NULL with workspace_bytes 0; the argument stays for a stable ABI). */
 int fa_blocksparse_fwd(const fa_desc* desc, const void* Q, const void* K, const void* V,
                        float scale, int causal, const int32_t* key_len,
                        const uint8_t* block_mask, int32_t block_size, void* O, float* LSE,
@@ -118,7 +121,8 @@ int fa_blocksparse_fwd(const fa_desc* desc, const void* Q, const void* K, const 
 
 /* Block-sparse backward: fa_bwd restricted to the kept blocks; needs the O and
  * LSE of fa_blocksparse_fwd with the same mask, causal flag and key lengths.
- * Same requirements. */
+ * Same requirements on the mask; `workspace` must hold
+ * fa_blocksparse_workspace_bytes(desc, bs, 1) bytes (= fa_bwd_workspace_bytes). */
 int fa_blocksparse_bwd(const fa_desc* desc, const void* Q, const void* K, const void* V,
                        const void* O, const void* dO, const float* LSE, float scale, int causal,
                        const int32_t* key_len, const uint8_t* block_mask, int32_t block_size,

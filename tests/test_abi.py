@@ -38,7 +38,7 @@ def test_library_exports_every_header_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.fa_version() == 102
+    assert lib.fa_version() == 103
     for code in (0, -1, -2, -3, -4):
         assert lib.fa_status_string(code)
     assert b"unknown" in lib.fa_status_string(7)
@@ -83,8 +83,18 @@ def test_argument_errors_before_any_launch(lib):
     for bs in (64, 100, 192, 512):
         assert lib.fa_blocksparse_fwd(ref(d), A, A, A, 0.1, 0, None, A, bs, A, A, A, 1 << 30, None) == -1
     assert lib.fa_blocksparse_fwd(ref(d), A, A, A, 0.1, 0, None, None, 128, A, A, A, 1 << 30, None) == -1
-    assert lib.fa_blocksparse_fwd(ref(d), A, A, A, 0.1, 1, None, A, 128, A, A, A, 16, None) == -3
     assert lib.fa_blocksparse_workspace_bytes(ref(d), 100, 0) == 0
+    # more than 1024 blocks per side is unsupported
+    big = _desc(B=1, H=1, N=128 * 1025)
+    assert lib.fa_blocksparse_fwd(ref(big), A, A, A, 0.1, 0, None, A, 128, A, A, None, 0, None) == -2
+    # the forward needs no workspace; the backward needs the fa_bwd one
+    need = lib.fa_bwd_workspace_bytes(ref(d))
+    assert lib.fa_blocksparse_workspace_bytes(ref(d), 128, 0) == 0
+    assert lib.fa_blocksparse_workspace_bytes(ref(d), 128, 1) == need
+    assert lib.fa_blocksparse_bwd(ref(d), A, A, A, A, A, A, 0.1, 1, None, A, 128, A, A, A, A, need - 1,
+                                  None) == -3
+    assert lib.fa_blocksparse_bwd(ref(d), A, A, A, A, A, A, 0.1, 1, None, A, 128, A, A, A, None, need,
+                                  None) == -3
 
 
 def test_workspace_is_linear_in_sequence_length(lib):
