@@ -190,6 +190,44 @@ def cpu_baseline(case, budget_s: float):
                       f"at full N={case.N}, d={case.d}; {el:.1f} s wall"}
 
 
+def cpu_table(budget_s: float):
+    """The float64 oracle per workload: forward and forward + backward wall time on whole heads (heads taken
+    across batches first, until the budget is used), extrapolated to all heads by head count. One JSON line
+    per workload."""
+    import oracle
+    import workloads
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    for name in ("C1", "C2", "C3", "C4a", "C4b", "C5"):
+        case = workloads.make_config(name)
+        heads = [(b, h) for h in range(case.H) for b in range(case.B)]
+        kw = dict(causal=case.causal, key_len=case.key_len, block_mask=case.block_mask,
+                  block_size=case.block_size)
+        fwd_only = workloads.CONFIGS[name].get("fwd_only", False)
+        timed = {}
+        for leg in (("fwd",) if fwd_only else ("fwd", "fwd+bwd")):
+            n, t0 = 0, time.perf_counter()
+            for bh in heads:
+                oracle.forward(case.q, case.k, case.v, float(case.scale), heads=[bh], **kw)
+                if leg == "fwd+bwd":
+                    oracle.backward(case.q, case.k, case.v, case.do, float(case.scale), heads=[bh], **kw)
+                n += 1
+                if time.perf_counter() - t0 >= budget_s:
+                    break
+            timed[leg] = ((time.perf_counter() - t0) / n * len(heads), n)
+        pairs = kept_pairs(case)
+        row = {"workload": name, "heads": len(heads), "cores": int(threads),
+               "fwd_s": round(timed["fwd"][0], 3), "fwd_heads_timed": timed["fwd"][1],
+               "fwd_gflops": round(4 * case.d * pairs / timed["fwd"][0] / 1e9, 2)}
+        if "fwd+bwd" in timed:
+            row.update({"step_s": round(timed["fwd+bwd"][0], 3), "step_heads_timed": timed["fwd+bwd"][1],
+                        "step_gflops": round(14 * case.d * pairs / timed["fwd+bwd"][0] / 1e9, 2)})
+        print(json.dumps(row), flush=True)
+
+
 def standard_attention_step(q, k, v, do, scale: float, causal: bool):
     """The pages' baseline for the memory / runtime comparison, not part of the path:
     standard attention as separate framework ops that materialise S and P in HBM
@@ -283,6 +321,8 @@ def main():
     ap.add_argument("--dropout", type=float, default=0.0,
                     help="dropout probability on P (dense workloads; 0: none, the headline step)")
     ap.add_argument("--calibrate-copy", action="store_true", help="only run a 1 GiB device copy (counter scale)")
+    ap.add_argument("--cpu-table", action="store_true",
+                    help="only time the float64 oracle (fwd, fwd + bwd) on every workload; --cpu-budget s per leg")
     ap.add_argument("--digest-counters", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
                                                            "COPY_WRITE_DIR"),
                     help="print per-kernel HBM traffic from rocprofv3 --pmc csv runs")
@@ -298,6 +338,9 @@ def main():
         return
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.cpu_table:
+        cpu_table(args.cpu_budget)
         return
     if args.gpus != 1:
         print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not supported",
