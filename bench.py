@@ -156,9 +156,17 @@ def digest_counters(fetch_dir: str, write_dir: str, copy_fetch_dir: str, copy_wr
                          "hbm_read_bytes": round(rd), "hbm_write_bytes": round(wr),
                          "hbm_bytes_per_launch": round(rd + wr), "algorithmic_bytes": algo.get(name),
                          "ratio_to_algorithmic": round((rd + wr) / algo[name], 3) if name in algo else None}
+    # Standard attention's HBM bytes for the same step: the three-op implementation with S, P (and dP, dS)
+    # written and read back at e bytes, fwd (4 N d + 4 N^2) e and bwd (8 N d + 7 N^2) e per head.
+    standard = B * H * (12 * N * d + 11 * N * N) * e
+    measured = sum(k["hbm_bytes_per_launch"] for k in kernels.values())
+    algorithmic = sum(v for v in algo.values())
     out = {"workload": workload, "sources_hash": sources_hash(),
            "calibration": {"copy_bytes": copy_bytes, "fetch_scale": round(kf, 4), "write_scale": round(kw, 4)},
-           "kernels": kernels}
+           "kernels": kernels,
+           "step": {"hbm_bytes_measured": round(measured), "algorithmic_bytes": algorithmic,
+                    "standard_attention_model_bytes": standard,
+                    "standard_over_measured": round(standard / measured, 2)}}
     print(json.dumps(out, indent=1), flush=True)
 
 
