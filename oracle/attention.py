@@ -80,7 +80,7 @@ def head_probabilities(q: np.ndarray, k: np.ndarray, scale: float, allowed: np.n
     s = float(scale) * (q @ k.T)
     s = np.where(allowed, s, -np.inf)
     m = s.max(axis=1)                       # row max; -inf for a row with no allowed key
-    empty = ~np.isfinite(m)
+    empty = m == -np.inf                    # (a NaN score keeps its row non-empty: NaN propagates)
     m_safe = np.where(empty, 0.0, m)
     e = np.exp(s - m_safe[:, None])         # exp(-inf) = 0 on masked entries
     l = e.sum(axis=1)
@@ -268,7 +268,7 @@ def backward_keys(Q, K, V, dO, scale, b, h, keys, causal=False, key_len=None, bl
         # the chosen keys' columns of P and dP (zero where a key is not kept for a row)
         s_k = float(scale) * (_f64(q_[r]) @ _f64(k_[keys]).T)
         with np.errstate(invalid="ignore"):
-            p_k = np.where(ok_k, np.exp(np.where(ok_k, s_k, 0.0) - np.where(np.isfinite(lse), lse, 0.0)[:, None]),
+            p_k = np.where(ok_k, np.exp(np.where(ok_k, s_k, 0.0) - np.where(lse == -np.inf, 0.0, lse)[:, None]),
                            0.0)
         dp_k = _f64(do_[r]) @ _f64(v_[keys]).T
         ds_k = p_k * (dp_k - dsum[:, None])

@@ -462,3 +462,23 @@ def test_dropout_finite_differences(mi):
             args_p[which], args_m[which] = xp, xm
             num[idx] = (loss(*args_p) - loss(*args_m)) / (2 * h)
         np.testing.assert_allclose(G, num, rtol=1e-7, atol=1e-9)
+
+
+@pytest.mark.parametrize("mask", ["causal", "key_len", "block"])
+def test_nan_key_poisons_exactly_the_rows_that_see_it(mask):
+    """A NaN in key j reaches exactly the rows allowed to see key j: their scores for j are
+    NaN, so their softmax (and O, LSE) is NaN; every other row masks j to -inf before the
+    softmax and is identical to a run with a finite key j."""
+    rng = np.random.default_rng(17)
+    N, d, j = 8, 4, 5
+    q, k, v = (rng.standard_normal((1, 1, N, d)) for _ in range(3))
+    kw = {"causal": dict(causal=True), "key_len": dict(key_len=np.array([j], np.int32)),
+          "block": dict(block_mask=np.array([[1, 0], [0, 1]], np.uint8), block_size=4)}[mask]
+    sees = {"causal": np.arange(N) >= j, "key_len": np.zeros(N, bool), "block": np.arange(N) >= 4}[mask]
+    k_nan = k.copy()
+    k_nan[0, 0, j, 0] = np.nan
+    o, lse = oracle.forward(q, k_nan, v, 0.5, **kw)
+    o_ref, lse_ref = oracle.forward(q, k, v, 0.5, **kw)
+    assert np.all(np.isnan(lse[0, 0, sees])) and np.all(np.isnan(o[0, 0, sees]))
+    np.testing.assert_array_equal(o[0, 0, ~sees], o_ref[0, 0, ~sees])
+    np.testing.assert_array_equal(lse[0, 0, ~sees], lse_ref[0, 0, ~sees])
