@@ -111,12 +111,27 @@ int check_desc(const fa_desc* d) {
   if (d->B < 1 || d->H < 1 || d->N < 1 || d->reserved != 0) return FA_ERR_INVALID;
   if (d->dtype != FA_BF16 && d->dtype != FA_F32) return FA_ERR_INVALID;
   if (d->d != 64 && d->d != 128) return FA_ERR_UNSUPPORTED;
-  const int64_t e = (int64_t)elem_bytes(d->dtype);
+  // Rows start 16-byte aligned: every stride is a multiple of 16 bytes (tested in
+  // elements, so that no product can overflow).
+  const int64_t align = 16 / (int64_t)elem_bytes(d->dtype);
   if (d->stride_n < d->d || d->stride_h < 1 || d->stride_b < 1) return FA_ERR_INVALID;
-  if ((d->stride_n * e) % 16 || (d->stride_h * e) % 16 || (d->stride_b * e) % 16) return FA_ERR_INVALID;
-  // grid and index limits of the kernels
+  if (d->stride_n % align || d->stride_h % align || d->stride_b % align) return FA_ERR_INVALID;
+  // The largest element offset, (B-1) stride_b + (H-1) stride_h + (N-1) stride_n + d, must
+  // be an address a device can hold (2^48 elements): the kernels form it in 64 bits.
+  int64_t span = d->d, part = 0;
+  if (__builtin_mul_overflow((int64_t)d->B - 1, d->stride_b, &part) || __builtin_add_overflow(span, part, &span) ||
+      __builtin_mul_overflow((int64_t)d->H - 1, d->stride_h, &part) || __builtin_add_overflow(span, part, &span) ||
+      __builtin_mul_overflow((int64_t)d->N - 1, d->stride_n, &part) || __builtin_add_overflow(span, part, &span) ||
+      span > ((int64_t)1 << 48))
+    return FA_ERR_INVALID;
+  // Grid and index limits of the kernels. B, H, N are positive int32, so B H < 2^62
+  // and, once B H <= 2^31 - 1, both products below stay under 2^62.
   const int64_t inst = (int64_t)d->B * d->H;
-  if (inst * ((d->N + 127) / 128) > 0x7FFFFFFFll) return FA_ERR_UNSUPPORTED;
+  if (inst > 0x7FFFFFFFll) return FA_ERR_UNSUPPORTED;
+  // The kernels index rows and tiles in 32-bit arithmetic (row + tile size, tile
+  // counts rounded up): N <= 2^30 keeps every such sum below 2^31.
+  if (d->N > (1 << 30)) return FA_ERR_UNSUPPORTED;
+  if (inst * (((int64_t)d->N + 127) / 128) > 0x7FFFFFFFll) return FA_ERR_UNSUPPORTED;
   if (inst * d->N > (int64_t)1 << 40) return FA_ERR_UNSUPPORTED;
   return FA_OK;
 }

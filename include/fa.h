@@ -20,8 +20,8 @@
  *   LSE is a contiguous float32 [B, H, N] array.
  * Pointers.  Every tensor, key_len, block_mask and workspace pointer is a
  *   DEVICE pointer owned by the caller; the library never allocates or frees
- *   device memory. Base pointers must be 16-byte aligned, and stride_n * (bytes
- *   per element) a multiple of 16. Outputs must not alias inputs.
+ *   device memory. Base pointers must be 16-byte aligned, and every stride times
+ *   the bytes per element a multiple of 16. Outputs must not alias inputs.
  * Streams.  `stream` is a hipStream_t (NULL = the default stream). Work is
  *   enqueued on it and the call returns without synchronising: inputs must stay
  *   alive, and outputs must not be read, until the stream reaches that point.
@@ -66,7 +66,8 @@ enum fa_status {
 enum fa_dtype { FA_BF16 = 0, FA_F32 = 1 };
 
 typedef struct fa_desc {
-  int32_t B, H, N, d; /* batch, heads, sequence length (>= 1), head dim (64 or 128) */
+  int32_t B, H, N, d; /* batch, heads, sequence length (1 .. 2^30), head dim (64 or 128);
+                          FA_ERR_UNSUPPORTED when B H >= 2^31, B H N > 2^40 or N > 2^30 */
   int32_t dtype;      /* FA_BF16 or FA_F32 */
   int32_t reserved;   /* must be 0 */
   int64_t stride_b, stride_h, stride_n; /* element strides; the d stride is 1 */
