@@ -84,18 +84,29 @@ def sources_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_for(kernel: str, workload: str):
-    """HBM bytes per launch measured by rocprofv3 counters, if taken on the current sources."""
+def _traffic_record(workload: str):
+    """The committed rocprofv3 HBM-counter digest of a workload, if taken on the current sources."""
     path = os.path.join(ROOT, "profiles", f"attention_kernels_{workload}_hbm_traffic.txt")
     if not os.path.exists(path):
         return None
     with open(path) as fh:
         text = fh.read()
     rec = json.loads(text[text.index("{"):])  # the JSON follows a short header
-    if rec.get("sources_hash") != sources_hash():
-        return None
-    k = rec.get("kernels", {}).get(kernel)
+    return rec if rec.get("sources_hash") == sources_hash() else None
+
+
+def traffic_for(kernel: str, workload: str):
+    """HBM bytes per launch measured by rocprofv3 counters, if taken on the current sources."""
+    rec = _traffic_record(workload)
+    k = None if rec is None else rec.get("kernels", {}).get(kernel)
     return None if k is None else k.get("hbm_bytes_per_launch")
+
+
+def step_traffic_for(workload: str):
+    """Measured HBM bytes of a whole step against the algorithmic bytes and the standard-attention
+    byte model, from the same digest (None if absent or stale)."""
+    rec = _traffic_record(workload)
+    return None if rec is None else rec.get("step")
 
 
 # Library timer names of the kernels, by a fragment of their symbol.
@@ -481,6 +492,7 @@ def main():
         "kernels": {k: {"mean_ms": round(v["mean_ms"], 4), "launches": v["launches"],
                         "share": round(v["share"], 4)} for k, v in kt.items()},
         "roofline": roofline,
+        "hbm_step": step_traffic_for(args.workload),
         "device_peak_bf16": {"value": device_peak_bf16_tflops(), "unit": "TFLOP/s",
                              "note": "reported peak engine clock x CUs x 4096 flop/clk/CU"},
     }
