@@ -635,25 +635,6 @@ void bwd_dq_kernel(BwdKParams p) {
     qf[kk] = *reinterpret_cast<const bf16x8*>(Qh + qoff + 16 * kk);
     df[kk] = *reinterpret_cast<const bf16x8*>(dOh + qoff + 16 * kk);
   }
-  // The row statistics the recomputation needs: D = sum_i dO_i O_i (this lane's
-  // half of the dims, then its partner lane's) and lse2 = LSE log2(e), or +inf
-  // when the row has no key so that recomputed probabilities are 0. The dK/dV
-  // pass, launched after this one, reads them from the workspace.
-  float d_half = 0.f;
-#pragma unroll
-  for (int kk = 0; kk < NKK; ++kk) {
-    const bf16x8 ov = *reinterpret_cast<const bf16x8*>(p.o + base + qoff + 16 * kk);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) d_half = fmaf((float)ov[i], (float)df[kk][i], d_half);
-  }
-  const float d_q = pair_sum(d_half);
-  const float lse_q = p.lse[rowbase + qc];
-  const float lse2_q = (lse_q == kNegInf) ? kPosInf : lse_q * kLog2e;
-  if (qrow < N && g == 0) {
-    p.delta[rowbase + qrow] = d_q;
-    p.lse2[rowbase + qrow] = lse2_q;
-  }
-
   f32x16 dqacc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
@@ -671,6 +652,27 @@ void bwd_dq_kernel(BwdKParams p) {
     cp.issue(vw, Vh, p.sn, kv0, N);
   };
   issue_tile(tile_kv0(0), bK0, bV0);
+
+  // The row statistics the recomputation needs, formed while the first tile's copies
+  // are in flight: D = sum_i dO_i O_i (this lane's half of the dims, then its partner
+  // lane's) and lse2 = LSE log2(e), or +inf when the row has no key so that
+  // recomputed probabilities are 0. The dK/dV pass, launched after this one, reads
+  // them from the workspace.
+  float d_half = 0.f;
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) {
+    const bf16x8 ov = *reinterpret_cast<const bf16x8*>(p.o + base + qoff + 16 * kk);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) d_half = fmaf((float)ov[i], (float)df[kk][i], d_half);
+  }
+  const float d_q = pair_sum(d_half);
+  const float lse_q = p.lse[rowbase + qc];
+  const float lse2_q = (lse_q == kNegInf) ? kPosInf : lse_q * kLog2e;
+  if (qrow < N && g == 0) {
+    p.delta[rowbase + qrow] = d_q;
+    p.lse2[rowbase + qrow] = lse2_q;
+  }
+
   wait_vmem();
   __syncthreads();
 
