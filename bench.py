@@ -336,7 +336,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--lib", default=None,
-                    help="load this build of the library instead of the package's (tile-size variants)")
+                    help="load this library file instead of the package's (tile-size variants)")
     ap.add_argument("--dropout", type=float, default=0.0,
                     help="dropout probability on P (dense workloads; 0: none, the headline step)")
     ap.add_argument("--calibrate-copy", action="store_true", help="only run a 1 GiB device copy (counter scale)")
@@ -362,7 +362,7 @@ def main():
         cpu_table(args.cpu_budget)
         return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not supported",
+        print(f"bench.py: the library runs on exactly one GPU; --gpus {args.gpus} is not supported",
               file=sys.stderr, flush=True)
         sys.exit(2)
 
