@@ -237,14 +237,18 @@ void bwd_dkdv_kernel(BwdKParams p) {
       // 2^(c S - lse2) = 0 there (c > 0).
       const bool need_mask =
           (!SPARSE || SMASK) && ((p.causal && q0 < kw0 + 31) || (kw0 + 32 > kv_len) || (q0 + BRQ > N));
+      // Register r of query block sb is query q0 + 4 g + off with off a compile-time
+      // constant: the entry is kept iff lo <= off <= hi (the lane's key is below kv_len
+      // and, when causal, at or before the query; the query is below N).
       auto mask_scores = [&](f32x16 (&s)[NQB]) __attribute__((always_inline)) {
+        const int lo = mykey < kv_len ? (p.causal ? mykey : 0) - q0 - 4 * g : 0x3FFFFFFF;
+        const int hi = N - 1 - q0 - 4 * g;
 #pragma unroll
         for (int sb = 0; sb < NQB; ++sb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int qi = q0 + 32 * sb + 8 * (r >> 2) + 4 * g + (r & 3);
-            const bool ok = mykey < kv_len && qi < N && (!p.causal || mykey <= qi);
-            if (!ok) s[sb][r] = kNegInf;
+            const int off = 32 * sb + 8 * (r >> 2) + (r & 3);
+            if (off < lo || off > hi) s[sb][r] = kNegInf;
           }
       };
 
@@ -685,12 +689,14 @@ void bwd_dq_kernel(BwdKParams p) {
     // dS^T = P^T (dP^T - D); register r of block kb is key kv0 + 32 kb + 8 (r/4) + 4 g + r%4.
     const bool need_mask = (!SPARSE || SMASK) && ((kv0 + BC > kv_len) || (p.causal && kv0 + BC - 1 > q0 + 32 * wave));
     // Masked entries of S become -inf, so that 2^(c S - lse2) = 0 there (c > 0).
+    // (A key is kept iff key <= min(kv_len - 1, qrow when causal); register r holds key
+    // kv0 + 32 kb + 4 g + off with off a compile-time constant: one compare per entry.)
     auto mask_block = [&](f32x16& s, int kb) __attribute__((always_inline)) {
+      const int lim = min(kv_len - 1, p.causal ? qrow : 0x3FFFFFFF) - kv0 - 32 * kb - 4 * g;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int key = kv0 + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
-        const bool ok = key < kv_len && (!p.causal || key <= qrow);
-        if (!ok) s[r] = kNegInf;
+        const int off = 8 * (r >> 2) + (r & 3);
+        if (off > lim) s[r] = kNegInf;
       }
     };
 
