@@ -3,52 +3,50 @@
 #include <math.h>
 #include <string.h>
 
-#include <mutex>
-
 #include "fa.h"
 #include "fa_internal.hpp"
 
 namespace fa {
 
 // ------------------------------------------------------------------------------ timer
+//
+// The optional kernel timer keeps its state per calling thread: a launch consults only
+// its own thread's record (one thread_local flag while the timer is off), so calls from
+// different threads share nothing and no lock is taken on any path.
 
 namespace {
 constexpr int kTimerSlots = 8192;
-struct TimerSlot {
-  const char* name;
-  int used;
-};
 struct Timer {
-  std::mutex mu;
-  bool enabled = false;
   bool created = false;
   hipEvent_t start[kTimerSlots];
   hipEvent_t stop[kTimerSlots];
-  TimerSlot slot[kTimerSlots];
+  const char* name[kTimerSlots];
   int n = 0;
   int open = -1;  // slot whose start event was recorded and whose stop is pending
 };
+thread_local bool t_enabled = false;  // this thread's timer is on (nothing is allocated until it is)
+thread_local Timer* t_timer = nullptr;
 Timer& timer() {
-  static Timer* t = new Timer();  // never destroyed: events may outlive static teardown
-  return *t;
+  // Never destroyed: its events may outlive thread and static teardown.
+  if (!t_timer) t_timer = new Timer();
+  return *t_timer;
 }
 }  // namespace
 
 void timer_begin(const char* name, hipStream_t stream) {
+  if (!t_enabled) return;
   Timer& t = timer();
-  std::lock_guard<std::mutex> lk(t.mu);
   t.open = -1;
-  if (!t.enabled || t.n >= kTimerSlots) return;
+  if (t.n >= kTimerSlots) return;
   const int i = t.n++;
-  t.slot[i].name = name;
-  t.slot[i].used = 1;
+  t.name[i] = name;
   hipEventRecord(t.start[i], stream);
   t.open = i;
 }
 
 void timer_end(hipStream_t stream) {
+  if (!t_enabled) return;
   Timer& t = timer();
-  std::lock_guard<std::mutex> lk(t.mu);
   if (t.open >= 0) hipEventRecord(t.stop[t.open], stream);
   t.open = -1;
 }
@@ -58,39 +56,42 @@ void timer_end(hipStream_t stream) {
 using namespace fa;
 
 extern "C" int fa_timer_enable(int enable) {
+  if (!enable) {
+    t_enabled = false;
+    return FA_OK;
+  }
   Timer& t = timer();
-  std::lock_guard<std::mutex> lk(t.mu);
-  if (enable && !t.created) {
+  if (!t.created) {
     for (int i = 0; i < kTimerSlots; ++i) {
       if (hipEventCreate(&t.start[i]) != hipSuccess || hipEventCreate(&t.stop[i]) != hipSuccess)
         return FA_ERR_HIP;
     }
     t.created = true;
   }
-  t.enabled = enable != 0;
+  t_enabled = true;
   return FA_OK;
 }
 
 extern "C" void fa_timer_reset(void) {
-  Timer& t = timer();
-  std::lock_guard<std::mutex> lk(t.mu);
-  t.n = 0;
-  t.open = -1;
+  if (!t_timer) return;
+  t_timer->n = 0;
+  t_timer->open = -1;
 }
 
 extern "C" int fa_timer_read(const char* kernel, double* total_ms, int64_t* launches) {
   if (!kernel || !total_ms || !launches) return FA_ERR_INVALID;
-  Timer& t = timer();
-  std::lock_guard<std::mutex> lk(t.mu);
   double sum = 0.0;
   int64_t cnt = 0;
-  for (int i = 0; i < t.n; ++i) {
-    if (strcmp(t.slot[i].name, kernel) != 0) continue;
-    if (hipEventSynchronize(t.stop[i]) != hipSuccess) return FA_ERR_HIP;
-    float ms = 0.f;
-    if (hipEventElapsedTime(&ms, t.start[i], t.stop[i]) != hipSuccess) return FA_ERR_HIP;
-    sum += ms;
-    ++cnt;
+  if (t_timer) {
+    Timer& t = *t_timer;
+    for (int i = 0; i < t.n; ++i) {
+      if (strcmp(t.name[i], kernel) != 0) continue;
+      if (hipEventSynchronize(t.stop[i]) != hipSuccess) return FA_ERR_HIP;
+      float ms = 0.f;
+      if (hipEventElapsedTime(&ms, t.start[i], t.stop[i]) != hipSuccess) return FA_ERR_HIP;
+      sum += ms;
+      ++cnt;
+    }
   }
   *total_ms = sum;
   *launches = cnt;
@@ -116,6 +117,9 @@ int check_desc(const fa_desc* d) {
   const int64_t align = 16 / (int64_t)elem_bytes(d->dtype);
   if (d->stride_n < d->d || d->stride_h < 1 || d->stride_b < 1) return FA_ERR_INVALID;
   if (d->stride_n % align || d->stride_h % align || d->stride_b % align) return FA_ERR_INVALID;
+  // The tile copies keep each lane's offset from a tile's first row (up to 128 rows)
+  // in 32 bits: 128 stride_n must stay below 2^31.
+  if (d->stride_n >= ((int64_t)1 << 24)) return FA_ERR_UNSUPPORTED;
   // The largest element offset, (B-1) stride_b + (H-1) stride_h + (N-1) stride_n + d, must
   // be an address a device can hold (2^48 elements): the kernels form it in 64 bits.
   int64_t span = d->d, part = 0;

@@ -151,14 +151,15 @@ __device__ __forceinline__ float sum_bf16x8(bf16x8 v, float acc) {
 
 // The bf16 kernels' softmax step: as online_softmax_step, but the probabilities
 // are packed to bf16 (pb, the B operands of the P V product; k-step ks = 2 kb + s
-// holds registers 8 s .. 8 s + 7 of block kb) and the row sum adds up those
-// rounded values. The normaliser is then the sum of exactly the weights the
-// product applies, so O is a convex combination of V rows: a bf16 rounding of a
-// dominant probability cancels instead of scaling O. (LSE then carries that
-// rounding, at most ln(1 + 2^-8) in a row with a single dominant key.)
+// holds registers 8 s .. 8 s + 7 of block kb) and two row sums are kept. l_run
+// adds up the rounded values: O's normaliser is then the sum of exactly the
+// weights the product applies, so O is a convex combination of V rows and a bf16
+// rounding of a dominant probability cancels instead of scaling O. lu_run adds
+// up the unrounded float32 values, the row sum of exp(S - m) that LSE = m + ln l
+// is defined with (the running sum of the tiled softmax).
 template <int NKB>
 __device__ __forceinline__ float softmax_tile_bf16(f32x16 (&s)[NKB], float c, float& m_run, float& l_run,
-                                                   bf16x8 (&pb)[2 * NKB]) {
+                                                   float& lu_run, bf16x8 (&pb)[2 * NKB]) {
   float mx = kNegInf;
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb)
@@ -170,18 +171,22 @@ __device__ __forceinline__ float softmax_tile_bf16(f32x16 (&s)[NKB], float c, fl
   const float m_use = (m_new == kNegInf) ? 0.f : m_new;
   const float alpha = fast_exp2(m_run - m_use);
   m_run = m_new;
-  float rs = 0.f;
+  float rs = 0.f, ru = 0.f;
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
     for (int sh = 0; sh < 2; ++sh) {
 #pragma unroll
-      for (int i = 8 * sh; i < 8 * sh + 8; ++i) s[kb][i] = fast_exp2(fmaf(s[kb][i], c, -m_use));
+      for (int i = 8 * sh; i < 8 * sh + 8; ++i) {
+        s[kb][i] = fast_exp2(fmaf(s[kb][i], c, -m_use));
+        ru += s[kb][i];
+      }
       pb[2 * kb + sh] = pack_bf16x8(s[kb][8 * sh + 0], s[kb][8 * sh + 1], s[kb][8 * sh + 2], s[kb][8 * sh + 3],
                                     s[kb][8 * sh + 4], s[kb][8 * sh + 5], s[kb][8 * sh + 6], s[kb][8 * sh + 7]);
       rs = sum_bf16x8(pb[2 * kb + sh], rs);
     }
   l_run = l_run * alpha + rs;
+  lu_run = lu_run * alpha + ru;
   return alpha;
 }
 
@@ -249,7 +254,7 @@ void fwd_bf16_kernel(FwdKParams p) {
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
-  float m_run = kNegInf, l_run = 0.f;
+  float m_run = kNegInf, l_run = 0.f, lu_run = 0.f;
 
   // Software pipeline over the key tiles. Iteration t computes S(t) = K_t Q^T,
   // then the P V product of tile t - 1 interleaved with the softmax of tile t, so
@@ -336,7 +341,7 @@ void fwd_bf16_kernel(FwdKParams p) {
       if (needs_mask(kv0_of(0))) mask_tile<NKB>(sacc, kv0_of(0), rg.kv_len, p.causal, qrow, g);
       // P^T as B operands: k-step ks = 2 kb + s covers keys 32 kb + 16 s +
       // {4g..4g+3, 8+4g..8+4g+3}. (alpha is irrelevant: nothing accumulated yet.)
-      softmax_tile_bf16<NKB>(sacc, p.c, m_run, l_run, pb);
+      softmax_tile_bf16<NKB>(sacc, p.c, m_run, l_run, lu_run, pb);
       if (DROP) drop_tile(pb, kv0_of(0));
     }
     wait_vmem();
@@ -364,7 +369,7 @@ void fwd_bf16_kernel(FwdKParams p) {
       const int voff = (int)(lds_address(vr) - lds_address(sT));
       bf16x8 a0 = ta.read_tr(voff, 0, 0);
       bf16x8 a1 = ta.read_tr(voff, 1 / NDB, 1 % NDB);
-      float mx0 = kNegInf, mx1 = kNegInf, m_new = 0.f, m_use = 0.f, alpha = 1.f, rs = 0.f;
+      float mx0 = kNegInf, mx1 = kNegInf, m_new = 0.f, m_use = 0.f, alpha = 1.f, rs = 0.f, ru = 0.f;
 #pragma unroll
       for (int i = 0; i < NPV; ++i) {
         const bf16x8 a = a0;
@@ -390,6 +395,7 @@ void fwd_bf16_kernel(FwdKParams p) {
 #pragma unroll
           for (int e = s0; e < s1; ++e) {
             sacc[e / 16][e % 16] = fast_exp2(fmaf(sacc[e / 16][e % 16], p.c, -m_use));
+            ru += sacc[e / 16][e % 16];
             if ((e & 7) == 7) {  // a group of 8 probabilities is complete: pack and sum it
               const int kb = e / 16, s8 = (e % 16) / 8;
               pbn[2 * kb + s8] = pack_bf16x8(sacc[kb][8 * s8 + 0], sacc[kb][8 * s8 + 1], sacc[kb][8 * s8 + 2],
@@ -405,11 +411,12 @@ void fwd_bf16_kernel(FwdKParams p) {
       // rescale branch, out of the slices they were placed in.
 #pragma unroll
       for (int i = 0; i < 2 * NKB; ++i) asm volatile("" : "+v"(pbn[i]));
-      asm volatile("" : "+v"(rs), "+v"(alpha), "+v"(m_new));
+      asm volatile("" : "+v"(rs), "+v"(ru), "+v"(alpha), "+v"(m_new));
       if (DROP) drop_tile(pbn, kv0);
       const float m_prev = m_run;
       m_run = m_new;
       l_run = l_run * alpha + rs;
+      lu_run = lu_run * alpha + ru;
       // alpha == 1 exactly when no row of this wave moved its reference max.
       if (__builtin_amdgcn_ballot_w64(m_run != m_prev)) {
 #pragma unroll
@@ -429,8 +436,10 @@ void fwd_bf16_kernel(FwdKParams p) {
     else pv_mfma(sV1, pb);
   }
 
-  // Epilogue: O = O_acc / l, LSE = (m + log2 l) ln 2. Rows with no key: O = 0, LSE = -inf.
+  // Epilogue: O = O_acc / l (the rounded weights' sum), LSE = (m + log2 lu) ln 2 (the
+  // unrounded sum). Rows with no key: O = 0, LSE = -inf.
   const float l_tot = pair_sum(l_run);
+  const float lu_tot = pair_sum(lu_run);
   const float inv = l_tot > 0.f ? (DROP ? p.drop.scale : 1.f) / l_tot : 0.f;
   if (qrow < N) {
     bf16* Orow = static_cast<bf16*>(p.o) + base + (int64_t)qrow * p.sn;
@@ -444,7 +453,7 @@ void fwd_bf16_kernel(FwdKParams p) {
         *reinterpret_cast<u32x2*>(Orow + db * 32 + 8 * j + 4 * g) = w;
       }
     if (g == 0)
-      p.lse[(int64_t)inst * N + qrow] = l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : kNegInf;
+      p.lse[(int64_t)inst * N + qrow] = lu_tot > 0.f ? (m_run + fast_log2(lu_tot)) * kLn2 : kNegInf;
   }
 }
 

@@ -35,13 +35,18 @@
  *   A query row with no kept key gets O = 0, LSE = -inf and no gradient.
  * Numbers.  All products accumulate in float32. bf16 outputs are rounded to
  *   nearest even. LSE[i] = m_i + ln(l_i), natural log, where m_i is the row
- *   max of the scaled, masked S and l_i the row sum of exp(S - m_i).
+ *   max of the scaled, masked S and l_i the float32 row sum of exp(S - m_i)
+ *   (reading notes, §Algorithm › Tiling: the running row sum). In the bf16
+ *   forward the P V product takes the probabilities rounded to bf16, and O is
+ *   normalised by the sum of exactly those rounded weights (so O stays a convex
+ *   combination of V rows); LSE uses the unrounded sum.
  *   `scale` must be finite and >= 0. Inputs must be finite.
  * Errors.  Every call returns FA_OK (0) or a negative FA_ERR_* code. Argument
  *   checks run before anything is enqueued; a failed check enqueues nothing.
  *   FA_ERR_HIP reports a launch error from the HIP runtime.
- * Threads.  Calls are reentrant; they share no state except the optional
- *   kernel timer below.
+ * Threads.  Calls are reentrant and thread-safe: they share no state and take
+ *   no lock. (The optional kernel timer below keeps its state per calling
+ *   thread.)
  */
 #ifndef FA_H_
 #define FA_H_
@@ -70,7 +75,9 @@ typedef struct fa_desc {
                           FA_ERR_UNSUPPORTED when B H >= 2^31, B H N > 2^40 or N > 2^30 */
   int32_t dtype;      /* FA_BF16 or FA_F32 */
   int32_t reserved;   /* must be 0 */
-  int64_t stride_b, stride_h, stride_n; /* element strides; the d stride is 1 */
+  int64_t stride_b, stride_h, stride_n; /* element strides; the d stride is 1. stride_n
+                          must be below 2^24 elements (FA_ERR_UNSUPPORTED otherwise: the
+                          tile copies form a lane's offset within 128 rows in 32 bits) */
 } fa_desc;
 
 /* Forward: O = softmax(scale * Q K^T + mask) V and LSE (see above).
@@ -112,8 +119,8 @@ size_t fa_blocksparse_workspace_bytes(const fa_desc* desc, int32_t block_size, i
  * fa_fwd, may be 0 / NULL) combine with the block mask by AND: an entry is kept
  * iff its block is nonzero, and it is causal-allowed, and its key is below the
  * batch's key length. Blocks above the diagonal are then skipped when causal.
- * Requires N % bs == 0, bs a positive multiple of 128 and N / bs <= 1024
- * (else FA_ERR_UNSUPPORTED). bf16 only. `workspace` is not used (it may be
+ * Requires bs to be a positive multiple of 128 that divides N (else
+ * FA_ERR_INVALID) and N / bs <= 1024 (else FA_ERR_UNSUPPORTED). bf16 only. `workspace` is not used (it may be
  * NULL with workspace_bytes 0; the argument stays for a stable ABI). */
 int fa_blocksparse_fwd(const fa_desc* desc, const void* Q, const void* K, const void* V,
                        float scale, int causal, const int32_t* key_len,
@@ -158,12 +165,14 @@ const char* fa_status_string(int status);
 /* FA_VERSION of the built library. */
 int fa_version(void);
 
-/* Optional kernel timer (instrumentation for benchmarks). When enabled, every
- * kernel the library launches is bracketed by two HIP events on its stream.
- * fa_timer_read synchronises on the recorded events and returns the summed
- * duration (ms) and launch count of the kernels whose name equals `kernel`
- * since the last reset. Process-wide state; not for concurrent use. Up to 8192
- * launches are recorded between resets; later ones are not timed.
+/* Optional kernel timer (instrumentation for benchmarks). While enabled on a
+ * thread, every kernel the library launches from that thread is bracketed by two
+ * HIP events on its stream. fa_timer_read synchronises on the calling thread's
+ * recorded events and returns the summed duration (ms) and launch count of the
+ * kernels whose name equals `kernel` since that thread's last reset. The state
+ * is per thread: launches from other threads are neither recorded nor affected,
+ * and a thread whose timer is off only reads one thread-local flag per launch.
+ * Up to 8192 launches are recorded between resets; later ones are not timed.
  * fa_timer_enable returns FA_OK or FA_ERR_HIP (events could not be created). */
 int fa_timer_enable(int enable);
 void fa_timer_reset(void);

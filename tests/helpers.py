@@ -15,14 +15,27 @@ import oracle  # noqa: E402
 import workloads  # noqa: E402
 
 # Tolerances: fp32 configs max |err| <= 1e-5 (O and LSE); bf16 configs max |err O| <= 2e-2 and
-# relative Frobenius error of dQ, dK, dV <= 5e-2. bf16 LSE max |err| <= 5e-3 (internal check, not
-# one of the graded bounds): the bf16 kernels normalise by the sum of the probabilities as rounded
-# to bf16 for the P V product, so a row dominated by one key carries that key's bf16 rounding,
-# |ln(1 + delta)| <= ln(1 + 2^-8) = 3.9e-3, in its LSE (plus float32 rounding).
+# relative Frobenius error of dQ, dK, dV <= 5e-2 over the compared tensor. Two internal checks on
+# top of those bounds:
+#  * bf16 LSE max |err| <= 1e-3: LSE is m + ln(l) with l the float32 row sum of the unrounded
+#    exponentials, so only float32 and exp2 rounding remain;
+#  * per 32-row slab of dQ, dK and dV (32 consecutive queries or keys of one instance; the last
+#    slab of a ragged N is shorter), relative Frobenius error <= 5e-2 of max(|ref_slab|,
+#    0.1 * RMS slab norm of the compared tensor). A missing or wrong slab scores about 1 and a
+#    single zeroed row of typical size about 1/sqrt(32) = 0.18, so both fail even where the
+#    whole-tensor norm would hide them. Slabs rather than single rows because D = rowsum(dO o O)
+#    is formed from the stored bf16 O, whose rounding moves D by an amount that does not shrink
+#    with the row's own gradient: rows whose exact gradient nearly cancels (causal row 0 of dQ
+#    is exactly 0; a very peaked softmax) carry a relative error of 0.1-0.25 on their own, while
+#    over a slab it averages against the neighbouring rows. The floor keeps slabs with a (near)
+#    zero gradient (keys no query sees) from turning rounding into a large relative error.
 TOL_F32 = 1e-5
 TOL_O_BF16 = 2e-2
-TOL_LSE_BF16 = 5e-3
+TOL_LSE_BF16 = 1e-3
 TOL_GRAD_FRO = 5e-2
+TOL_GRAD_SLAB = 5e-2
+SLAB_FLOOR = 0.1
+SLAB = 32
 
 
 def ensure_library():
@@ -78,13 +91,13 @@ def oracle_kwargs(case: workloads.Case):
                 block_size=case.block_size)
 
 
-def run_oracle(case: workloads.Case, backward: bool = True, heads=None):
+def run_oracle(case: workloads.Case, backward: bool = True, heads=None, dropout=None):
     sc = float(case.scale)
     kw = oracle_kwargs(case)
-    O, LSE = oracle.forward(case.q, case.k, case.v, sc, heads=heads, **kw)
+    O, LSE = oracle.forward(case.q, case.k, case.v, sc, heads=heads, dropout=dropout, **kw)
     out = {"o": O, "lse": LSE}
     if backward:
-        dQ, dK, dV = oracle.backward(case.q, case.k, case.v, case.do, sc, heads=heads, **kw)
+        dQ, dK, dV = oracle.backward(case.q, case.k, case.v, case.do, sc, heads=heads, dropout=dropout, **kw)
         out.update(dq=dQ, dk=dK, dv=dV)
     return out
 
@@ -92,6 +105,22 @@ def run_oracle(case: workloads.Case, backward: bool = True, heads=None):
 def rel_fro(a, ref):
     den = np.linalg.norm(ref)
     return np.linalg.norm(a - ref) / (den if den > 0 else 1.0)
+
+
+def slab_errors(g, r, slab: int = SLAB):
+    """Relative Frobenius error of each run of `slab` consecutive rows of a [..., N, d] gradient,
+    per instance: |g_slab - r_slab| / max(|r_slab|, SLAB_FLOOR * RMS slab norm)."""
+    N, d = g.shape[-2], g.shape[-1]
+    g3 = g.reshape(-1, N, d)
+    r3 = r.reshape(-1, N, d)
+    err, ref = [], []
+    for s0 in range(0, N, slab):
+        err.append(np.linalg.norm((g3[:, s0:s0 + slab] - r3[:, s0:s0 + slab]).reshape(g3.shape[0], -1), axis=1))
+        ref.append(np.linalg.norm(r3[:, s0:s0 + slab].reshape(r3.shape[0], -1), axis=1))
+    err, ref = np.stack(err, axis=1), np.stack(ref, axis=1)
+    rms = float(np.sqrt(np.mean(ref ** 2))) if ref.size else 0.0
+    den = np.maximum(ref, SLAB_FLOOR * rms)
+    return np.where(den > 0, err / np.where(den > 0, den, 1.0), err)
 
 
 def compare(gpu, ref, case: workloads.Case, heads=None, backward=True):
@@ -115,5 +144,9 @@ def compare(gpu, ref, case: workloads.Case, heads=None, backward=True):
     if backward:
         for name in ("dq", "dk", "dv"):
             errs[name] = float(rel_fro(gpu[name][sel], ref[name][sel]))
+            se = slab_errors(gpu[name][sel], ref[name][sel])
+            errs[name + "_slab"] = float(se.max()) if se.size else 0.0
+        for name in ("dq", "dk", "dv"):
             assert errs[name] <= TOL_GRAD_FRO, errs
+            assert errs[name + "_slab"] <= TOL_GRAD_SLAB, errs
     return errs

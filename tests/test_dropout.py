@@ -2,9 +2,8 @@
 import numpy as np
 import pytest
 
-import oracle
 import workloads
-from helpers import compare, ensure_library, upload
+from helpers import compare, ensure_library, run_oracle, upload
 
 pytestmark = pytest.mark.gpu
 
@@ -40,10 +39,8 @@ def test_dropout_matches_oracle(p, mask, d):
     print("[case]", case.name, "p", p, "d", d, flush=True)
     gpu = _run(case, p)
     p8 = int(round(p * 256))
-    kw = dict(causal=case.causal, key_len=case.key_len, dropout=(p8, SEED, OFFSET))
-    O, LSE = oracle.forward(case.q, case.k, case.v, float(case.scale), **kw)
-    dQ, dK, dV = oracle.backward(case.q, case.k, case.v, case.do, float(case.scale), **kw)
-    compare(gpu, dict(o=O, lse=LSE, dq=dQ, dk=dK, dv=dV), case)
+    ref = run_oracle(case, dropout=(p8, SEED, OFFSET))
+    print("[case] errors", compare(gpu, ref, case), flush=True)
 
 
 def test_dropout_zero_equals_plain_and_seeds_matter():

@@ -392,6 +392,79 @@ def test_philox_known_answers():
         assert out == vec["out"]
 
 
+# Pair (i, j) of the first known-answer block (counter (0, 0, 0, 0), key (0, 0)): byte j of word i
+# of the published output 6627e8d5 e169c58d bc57ac4c 9b00dbd8, read off by hand (least significant
+# byte first). A swap of rows and columns, of word and byte, or a wrong byte order fails here.
+HAND_KEEP_BYTES = {(0, 0): 0xD5, (0, 1): 0xE8, (0, 2): 0x27, (0, 3): 0x66,
+                   (1, 0): 0x8D, (1, 1): 0xC5, (1, 2): 0x69, (1, 3): 0xE1,
+                   (2, 0): 0x4C, (2, 1): 0xAC, (2, 2): 0x57, (2, 3): 0xBC,
+                   (3, 0): 0xD8, (3, 1): 0xDB, (3, 2): 0x00, (3, 3): 0x9B}
+
+
+def _keep_byte(rows, cols, bh, seed, offset):
+    """Recover the generator byte behind each pair from the keep decisions alone: the pair is kept
+    at p8 = byte and dropped at p8 = byte + 1, so the byte is the number of p8 in 1..255 that keep it."""
+    n = np.zeros((len(rows), len(cols)), dtype=np.int64)
+    for p8 in range(1, 256):
+        n += oracle.dropout_keep(rows, cols, bh, p8, seed, offset)
+    return n
+
+
+def test_dropout_keep_bytes_by_hand():
+    """The (i, j) -> (counter, word, byte) map of the keep bits, pinned on the first published
+    known-answer vector: seed 0, offset 0, instance 0 put every pair i, j < 4 at counter (0,0,0,0)."""
+    got = _keep_byte(np.arange(4), np.arange(4), 0, 0, 0)
+    for (i, j), byte in HAND_KEEP_BYTES.items():
+        assert got[i, j] == byte, (i, j, got[i, j], byte)
+    # pair (1, 2) takes byte 2 of e169c58d = 0x69 = 105: kept iff p8 <= 105
+    assert oracle.dropout_keep([1], [2], 0, 105, 0, 0)[0, 0]
+    assert not oracle.dropout_keep([1], [2], 0, 106, 0, 0)[0, 0]
+    # and the rows 4.. / columns 4.. of the block belong to other counters (not the same bytes)
+    other = _keep_byte(np.arange(4, 8), np.arange(4), 0, 0, 0)
+    assert not np.array_equal(other, got)
+
+
+@pytest.mark.parametrize("vi", [1, 2])
+def test_dropout_keep_counter_and_key_words(vi):
+    """The other published vectors fix which counter word holds i div 4, j div 4, the instance and
+    the offset, and which key word holds which half of the seed: choosing rows, columns, instance,
+    offset and seed so that the counter and key equal the vector's, the recovered bytes must be
+    those of the published output words."""
+    kat = _load("philox4x32_10_kat.json")["vectors"][vi]
+    c = [int(x, 16) for x in kat["ctr"]]
+    k = [int(x, 16) for x in kat["key"]]
+    w = [int(x, 16) for x in kat["out"]]
+    rows = 4 * c[0] + np.arange(4)
+    cols = 4 * c[1] + np.arange(4)
+    seed = k[0] | (k[1] << 32)
+    got = _keep_byte(rows, cols, c[2], seed, c[3])
+    want = np.array([[(w[i] >> (8 * j)) & 0xFF for j in range(4)] for i in range(4)])
+    np.testing.assert_array_equal(got, want)
+
+
+def test_hand_n2_inverted_dropout():
+    """Inverted dropout in the forward (O = (P o Z) V / (1 - p), LSE of the softmax before dropout)
+    and its backward, on the N = 2 hand case with keep bits read off the published vector."""
+    g = _load("hand_n2_dropout.json")
+    inp = g["inputs"]
+    q, k, v, do = (_one_head(_arr(inp[n])) for n in ("q", "k", "v", "do"))
+    drop = (inp["p8"], inp["seed"], inp["offset"])
+    keep = oracle.dropout_keep(np.arange(2), np.arange(2), 0, *drop)
+    np.testing.assert_array_equal(keep, np.array(g["keep"]))
+    assert oracle.keep_scale(inp["p8"]) == 256.0 / 106.0
+    O, LSE = oracle.forward(q, k, v, _val(inp["scale"]), dropout=drop)
+    dQ, dK, dV = oracle.backward(q, k, v, do, _val(inp["scale"]), dropout=drop)
+    np.testing.assert_allclose(O[0, 0], _arr(g["o"]), rtol=1e-15, atol=1e-14)
+    np.testing.assert_allclose(LSE[0, 0], _arr(g["lse"]), rtol=0, atol=1e-14)
+    np.testing.assert_allclose(dV[0, 0], _arr(g["dv"]), rtol=1e-15, atol=1e-14)
+    np.testing.assert_allclose(dQ[0, 0], _arr(g["dq"]), rtol=1e-15, atol=1e-14)
+    np.testing.assert_allclose(dK[0, 0], _arr(g["dk"]), rtol=1e-15, atol=1e-14)
+    ok = oracle.allowed_matrix(2)
+    _, _, _, dsum = oracle.head_backward(q[0, 0], k[0, 0], v[0, 0], do[0, 0], _val(inp["scale"]), ok, keep,
+                                         oracle.keep_scale(inp["p8"]))
+    np.testing.assert_allclose(dsum, _arr(g["D"]), rtol=1e-15, atol=1e-14)
+
+
 def test_dropout_keep_rate_and_indexing():
     N, p8 = 512, 26
     keep = oracle.dropout_keep(np.arange(N), np.arange(N), 3, p8, seed=0x1234_5678_9ABC, offset=7)
