@@ -20,7 +20,7 @@ from typing import Optional
 
 from ._lib import (FA_BF16, FA_F32, FA_OK, FAError, FaDesc, lib)  # noqa: F401
 
-__all__ = ["fwd", "bwd", "blocksparse_fwd", "blocksparse_bwd", "bwd_workspace_bytes",
+__all__ = ["fwd", "bwd", "bwd_noalloc", "blocksparse_fwd", "blocksparse_bwd", "bwd_workspace_bytes",
            "blocksparse_workspace_bytes", "FAError", "lib", "KernelTimer"]
 
 
@@ -159,6 +159,22 @@ def bwd(q, k, v, o, do, lse, scale=None, causal=False, key_len=None, dq=None, dk
                       lse.data_ptr(), _scale(scale, q.shape[-1]), int(bool(causal)), _ptr(kl), dq.data_ptr(),
                       dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), ws.numel() * ws.element_size(), _stream(q))
     _check(st, "fa_bwd")
+    return dq, dk, dv
+
+
+def bwd_noalloc(q, k, v, o, do, lse, dq, dk, dv, scale=None, causal=False, key_len=None):
+    """fa_bwd_noalloc: the backward with its workspace in the library's static per-device scratch
+    (no allocation anywhere; the caller passes the outputs dq, dk, dv). Calls that overlap on one
+    GPU race on that scratch."""
+    d = _desc(q)
+    _same_layout(q, k, v, o, do)
+    _same_layout(q, dq, dk, dv)
+    _lse_check(lse, q)
+    kl = _key_len(key_len, q)
+    st = lib().fa_bwd_noalloc(ctypes.byref(d), q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                              do.data_ptr(), lse.data_ptr(), _scale(scale, q.shape[-1]), int(bool(causal)),
+                              _ptr(kl), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), _stream(q))
+    _check(st, "fa_bwd_noalloc")
     return dq, dk, dv
 
 

@@ -3,6 +3,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "fa.h"
 #include "fa_internal.hpp"
 
@@ -40,14 +42,14 @@ void timer_begin(const char* name, hipStream_t stream) {
   if (t.n >= kTimerSlots) return;
   const int i = t.n++;
   t.name[i] = name;
-  hipEventRecord(t.start[i], stream);
+  (void)hipEventRecord(t.start[i], stream);
   t.open = i;
 }
 
 void timer_end(hipStream_t stream) {
   if (!t_enabled) return;
   Timer& t = timer();
-  if (t.open >= 0) hipEventRecord(t.stop[t.open], stream);
+  if (t.open >= 0) (void)hipEventRecord(t.stop[t.open], stream);
   t.open = -1;
 }
 
@@ -233,6 +235,8 @@ extern "C" const char* fa_status_string(int status) {
     case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: head dim, dtype or size not supported by this call";
     case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing or too small";
     case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime reported an error";
+    case FA_ERR_SCRATCH:
+      return "FA_ERR_SCRATCH: the problem needs more workspace than the static scratch of fa_bwd_noalloc holds";
     default: return "unknown status";
   }
 }
@@ -264,6 +268,58 @@ extern "C" int fa_bwd(const fa_desc* desc, const void* Q, const void* K, const v
   if (!workspace || !aligned16(workspace) || workspace_bytes < bwd_ws_bytes(desc)) return FA_ERR_WORKSPACE;
   BwdArgs a = bwd_args(desc, Q, K, V, O, dO, LSE, scale, causal, key_len, dQ, dK, dV);
   carve_bwd(desc, workspace, a);
+  return hip_status(launch_bwd_bf16(a, static_cast<hipStream_t>(stream)));
+}
+
+// ------------------------------------------------------------------------------ no-alloc backward
+//
+// fa_bwd_noalloc: fa_bwd with its workspace (D and lse2, 8 bytes per row) in a static
+// device array instead of a caller buffer, for callers that cannot allocate. The array's
+// name is a host-side stand-in; its device address is looked up once per device with
+// hipGetSymbolAddress (with that device current) and only that address is passed on.
+
+namespace {
+constexpr size_t kScratchBytes = size_t{16} << 20;  // 16 MiB per device
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];  // device address of `scratch`, per device (null: not looked up)
+
+// The current device's address of `scratch`, or null with *err set.
+void* scratch_for_current_device(int* err) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    *err = FA_ERR_HIP;
+    return nullptr;
+  }
+  void* ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (ptr) return ptr;
+  // Looked up on the first call on this device (the lookup is idempotent, so two threads
+  // racing here store the same address).
+  if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+    *err = FA_ERR_HIP;
+    return nullptr;
+  }
+  g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+  return ptr;
+}
+}  // namespace
+
+extern "C" int fa_bwd_noalloc(const fa_desc* desc, const void* Q, const void* K, const void* V, const void* O,
+                              const void* dO, const float* LSE, float scale, int causal, const int32_t* key_len,
+                              void* dQ, void* dK, void* dV, void* stream) {
+  int st = check_desc(desc);
+  if (st) return st;
+  if (desc->dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if ((st = check_scale(scale))) return st;
+  if ((st = check_ptrs({Q, K, V, O, dO, LSE, dQ, dK, dV}))) return st;
+  if (bwd_ws_bytes(desc) > kScratchBytes) return FA_ERR_SCRATCH;
+  void* ws = scratch_for_current_device(&st);
+  if (!ws) return st;
+  BwdArgs a = bwd_args(desc, Q, K, V, O, dO, LSE, scale, causal, key_len, dQ, dK, dV);
+  // Every workspace entry is written by the first backward kernel before the second reads it,
+  // so nothing has to be cleared between calls.
+  carve_bwd(desc, ws, a);
   return hip_status(launch_bwd_bf16(a, static_cast<hipStream_t>(stream)));
 }
 

@@ -65,7 +65,8 @@ enum fa_status {
   FA_ERR_INVALID = -1,     /* null pointer, bad shape, stride, alignment or scale */
   FA_ERR_UNSUPPORTED = -2, /* d not in {64, 128}, or dtype not built for this call */
   FA_ERR_WORKSPACE = -3,   /* workspace pointer null or smaller than required */
-  FA_ERR_HIP = -4          /* the HIP runtime reported an error at launch */
+  FA_ERR_HIP = -4,         /* the HIP runtime reported an error at launch */
+  FA_ERR_SCRATCH = -5      /* fa_bwd_noalloc: more workspace than its static scratch holds */
 };
 
 enum fa_dtype { FA_BF16 = 0, FA_F32 = 1 };
@@ -158,6 +159,24 @@ int fa_bwd_dropout(const fa_desc* desc, const void* Q, const void* K, const void
                    const void* dO, const float* LSE, float scale, int causal, const int32_t* key_len,
                    float dropout_p, uint64_t seed, uint32_t offset, void* dQ, void* dK, void* dV,
                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Backward without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): fa_bwd with its workspace (8 bytes per row of B H N) taken from a
+ * static device array of 16 MiB that the library holds on each device it runs on
+ * until the process ends. The caller still passes every input and output. Same
+ * arguments, checks and results as fa_bwd (bit for bit); allocates nothing and
+ * calls no allocating routine. Problems with B H N > 2^21 rows (the workspace
+ * of fa_bwd_workspace_bytes above 16 MiB) return FA_ERR_SCRATCH before anything
+ * is enqueued. All calls on one
+ * device share that device's array: calls that overlap on one GPU (two streams,
+ * or two threads, without ordering between them) race on it and must be
+ * serialised by the caller. Nothing in the array needs to start at zero (each
+ * call writes every entry it reads). The array's device address is looked up on
+ * the first call on each device (hipGetSymbolAddress; FA_ERR_HIP if it fails). */
+int fa_bwd_noalloc(const fa_desc* desc, const void* Q, const void* K, const void* V, const void* O,
+                   const void* dO, const float* LSE, float scale, int causal, const int32_t* key_len,
+                   void* dQ, void* dK, void* dV, void* stream);
 
 /* Static, human-readable name of a status code. */
 const char* fa_status_string(int status);

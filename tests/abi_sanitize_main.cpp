@@ -47,7 +47,7 @@ int main() {
   const fa_desc d = desc();
 
   expect("version", fa_version(), FA_VERSION);
-  for (int s = -6; s <= 1; ++s) {
+  for (int s = -7; s <= 1; ++s) {
     const char* t = fa_status_string(s);
     if (!t || !*t) {
       std::fprintf(stderr, "status string %d empty\n", s);
@@ -128,6 +128,21 @@ int main() {
          FA_ERR_WORKSPACE);
   expect("bwd null dO", fa_bwd(&d, A, A, A, A, nullptr, F, 0.1f, 0, nullptr, A, A, A, A, need, nullptr),
          FA_ERR_INVALID);
+
+  // No-alloc backward: the same checks as fa_bwd, then the static scratch's size limit (2^21
+  // rows), all before the scratch's device address is looked up.
+  expect("bwd noalloc fp32", fa_bwd_noalloc(&f32, A, A, A, A, A, F, 0.1f, 0, nullptr, A, A, A, nullptr),
+         FA_ERR_UNSUPPORTED);
+  expect("bwd noalloc null dQ", fa_bwd_noalloc(&d, A, A, A, A, A, F, 0.1f, 0, nullptr, nullptr, A, A, nullptr),
+         FA_ERR_INVALID);
+  expect("bwd noalloc nan scale", fa_bwd_noalloc(&d, A, A, A, A, A, F, std::nanf(""), 0, nullptr, A, A, A, nullptr),
+         FA_ERR_INVALID);
+  const fa_desc rows_over = desc(1, 1, (1 << 21) + 1, 64);
+  expect("bwd noalloc 2^21 + 1 rows", fa_bwd_noalloc(&rows_over, A, A, A, A, A, F, 0.1f, 0, nullptr, A, A, A, nullptr),
+         FA_ERR_SCRATCH);
+  const fa_desc rows_over2 = desc(4, 8, 65537, 128);
+  expect("bwd noalloc 4 x 8 x 65537 rows", fa_bwd_noalloc(&rows_over2, A, A, A, A, A, F, 0.1f, 1, nullptr, A, A, A,
+                                                           nullptr), FA_ERR_SCRATCH);
 
   // Dropout: probability range, fp32.
   const float bad_p[] = {-0.1f, 1.0f, 1.5f, std::nanf(""), 0.999f};

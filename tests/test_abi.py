@@ -39,7 +39,7 @@ def test_library_exports_every_header_symbol(lib):
 
 def test_version_and_status_strings(lib):
     assert lib.fa_version() == 103
-    for code in (0, -1, -2, -3, -4):
+    for code in (0, -1, -2, -3, -4, -5):
         assert lib.fa_status_string(code)
     assert b"unknown" in lib.fa_status_string(7)
 
@@ -95,6 +95,21 @@ def test_argument_errors_before_any_launch(lib):
                                   None) == -3
     assert lib.fa_blocksparse_bwd(ref(d), A, A, A, A, A, A, 0.1, 1, None, A, 128, A, A, A, None, need,
                                   None) == -3
+
+
+def test_noalloc_backward_checks_before_any_launch(lib):
+    """fa_bwd_noalloc rejects what fa_bwd rejects, and problems beyond its static scratch (2^21 rows)
+    with FA_ERR_SCRATCH, all before touching the GPU."""
+    ref = ctypes.byref
+    d = _desc()
+    assert lib.fa_bwd_noalloc(ref(_desc(dtype=1)), A, A, A, A, A, A, 0.1, 0, None, A, A, A, None) == -2
+    assert lib.fa_bwd_noalloc(ref(d), A, A, A, A, A, A, 0.1, 0, None, None, A, A, None) == -1
+    assert lib.fa_bwd_noalloc(ref(d), A, A, A, A, A, A, -1.0, 0, None, A, A, A, None) == -1
+    assert lib.fa_bwd_noalloc(ref(_desc(B=1, H=1, N=(1 << 21) + 1)), A, A, A, A, A, A, 0.1, 0, None, A, A, A,
+                              None) == -5
+    assert lib.fa_bwd_noalloc(ref(_desc(B=2, H=16, N=65537, d=128)), A, A, A, A, A, A, 0.1, 1, None, A, A, A,
+                              None) == -5
+    assert b"FA_ERR_SCRATCH" in lib.fa_status_string(-5)
 
 
 def test_workspace_is_linear_in_sequence_length(lib):
