@@ -102,6 +102,61 @@ def traffic_for(kernel: str, workload: str):
     return None if k is None else k.get("hbm_bytes_per_launch")
 
 
+def _sq_record(workload: str):
+    """The committed rocprofv3 SQ-counter digest of a workload, if taken on the current sources."""
+    path = os.path.join(ROOT, "profiles", f"attention_kernels_{workload}_sq_counters.txt")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        text = fh.read()
+    if "{" not in text:
+        return None
+    rec = json.loads(text[text.index("{"):])
+    return rec if rec.get("sources_hash") == sources_hash() else None
+
+
+def counter_source(kind: str, workload: str, rec) -> str:
+    return (f"profiles/attention_kernels_{workload}_{kind}.txt: rocprofv3 counters from a separate run of the "
+            f"same command on one MI355X (not this run's box), kernel sources_hash {rec['sources_hash']}")
+
+
+def digest_sq(p1: str, p2: str, workload: str):
+    """Per-kernel SQ counter summary from two rocprofv3 --pmc csv runs (the two counter sets of the
+    profile's header): the matrix cores' busy fraction, where the waves' time goes, and instructions
+    per MFMA. Prints the text and the JSON that bench.py reads."""
+    import csv
+    import glob
+    import re
+    vals = {}
+    for d in (p1, p2):
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(f) as fh:
+                for row in csv.DictReader(fh):
+                    k = re.sub(r"^void fa::", "", row["Kernel_Name"])
+                    k = k.replace("(fa::FwdKParams)", "").replace("(fa::BwdKParams)", "")
+                    vals.setdefault(k, {}).setdefault(row["Counter_Name"], []).append(float(row["Counter_Value"]))
+    out = {"workload": workload, "sources_hash": sources_hash(), "kernels": {}}
+    for k, cs in vals.items():
+        name = next((v for frag, v in KERNEL_NAMES.items() if frag in k), None)
+        if name is None:
+            continue
+        m = {c: sum(v) / len(v) for c, v in cs.items()}
+        busy = (m["SQ_VALU_MFMA_BUSY_CYCLES"] / 1024) / (m["GRBM_GUI_ACTIVE"] / 8)
+        w, mf = m["SQ_WAVE_CYCLES"], m["SQ_INSTS_MFMA"]
+        rec = {"symbol": k, "mfma_busy": round(busy, 3), "issuing": round(m["SQ_ACTIVE_INST_ANY"] / w, 3),
+               "waiting": round(m["SQ_WAIT_ANY"] / w, 3), "issue_stalled": round(m["SQ_WAIT_INST_ANY"] / w, 3),
+               "valu_per_mfma": round((m["SQ_INSTS_VALU"] - mf) / mf, 2), "lds_per_mfma": round(m["SQ_INSTS_LDS"] / mf, 2),
+               "salu_per_mfma": round(m["SQ_INSTS_SALU"] / mf, 2), "lds_bank_conflicts": m["SQ_LDS_BANK_CONFLICT"]}
+        out["kernels"][name] = rec
+        print(k)
+        print("  " + "  ".join(f"{c}={m[c]:.4g}" for c in sorted(m)))
+        print(f"  mfma_busy {busy:.3f}; wave time: issuing {rec['issuing']:.2f}, waiting {rec['waiting']:.2f}, "
+              f"issue-stalled {rec['issue_stalled']:.2f}; per MFMA: {rec['valu_per_mfma']:.2f} other VALU, "
+              f"{rec['lds_per_mfma']:.2f} LDS, {rec['salu_per_mfma']:.2f} SALU; LDS bank conflicts "
+              f"{m['SQ_LDS_BANK_CONFLICT']:.0f}\n", flush=True)
+    print(json.dumps(out, indent=1), flush=True)
+
+
 def step_traffic_for(workload: str):
     """Measured HBM bytes of a whole step against the algorithmic bytes and the standard-attention
     byte model, from the same digest (None if absent or stale)."""
@@ -181,8 +236,34 @@ def digest_counters(fetch_dir: str, write_dir: str, copy_fetch_dir: str, copy_wr
     print(json.dumps(out, indent=1), flush=True)
 
 
-def cpu_baseline(case, budget_s: float):
-    """Time the float64 oracle (fwd + bwd) on whole heads of the workload until the budget is used."""
+def _parity_of(gpu, ref, bh):
+    """Errors of one instance's GPU outputs against the oracle's (host arithmetic only), with the bf16
+    bounds: O max abs <= 2e-2, dQ / dK / dV relative Frobenius <= 5e-2 (also per 32-row slab of
+    max(|slab|, 0.1 RMS slab norm)); LSE max abs <= 1e-3 as an internal check."""
+    import numpy as np
+    b, h = bh
+    e = {}
+    fin = np.isfinite(ref["lse"][b, h])
+    e["o_max_abs"] = float(np.max(np.abs(gpu["o"] - ref["o"][b, h])))
+    e["lse_max_abs"] = float(np.max(np.abs(gpu["lse"][fin] - ref["lse"][b, h][fin]))) if fin.any() else 0.0
+    ok = e["o_max_abs"] <= 2e-2 and e["lse_max_abs"] <= 1e-3
+    for n in ("dq", "dk", "dv"):
+        g, r = gpu[n], ref[n][b, h]
+        e[n + "_rel_fro"] = float(np.linalg.norm(g - r) / max(np.linalg.norm(r), 1e-300))
+        nslab = (r.shape[0] + 31) // 32
+        err = np.array([np.linalg.norm(g[32 * i:32 * i + 32] - r[32 * i:32 * i + 32]) for i in range(nslab)])
+        ref_n = np.array([np.linalg.norm(r[32 * i:32 * i + 32]) for i in range(nslab)])
+        den = np.maximum(ref_n, 0.1 * np.sqrt(np.mean(ref_n ** 2)))
+        e[n + "_worst_slab"] = float(np.max(err / np.where(den > 0, den, 1.0)))
+        ok = ok and e[n + "_rel_fro"] <= 5e-2 and e[n + "_worst_slab"] <= 5e-2
+    e["within_tolerance"] = bool(ok and np.all(np.isfinite(gpu["o"])))
+    return e
+
+
+def cpu_baseline(case, budget_s: float, gpu_instance=None):
+    """Time the float64 oracle (fwd + bwd) on whole heads of the workload until the budget is used.
+    gpu_instance(b, h) -> the benched step's outputs of that instance (host arrays o, lse, dq, dk, dv):
+    the oracle's outputs of the first timed instance are checked against them (parity of the run)."""
     import numpy as np
     import oracle
     try:
@@ -190,23 +271,31 @@ def cpu_baseline(case, budget_s: float):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         threads = os.cpu_count() or 1
-    heads = [(b, h) for b in range(case.B) for h in range(case.H)]
-    done = []
+    # the first and the last instance of the launch first, then the rest in order
+    n_inst = case.B * case.H
+    order = [0, n_inst - 1] + list(range(1, n_inst - 1)) if n_inst > 1 else [0]
+    heads = [(i // case.H, i % case.H) for i in order]
+    done, parity = [], []
     t0 = time.perf_counter()
     for bh in heads:
-        oracle.forward(case.q, case.k, case.v, float(case.scale), causal=case.causal, key_len=case.key_len,
-                       block_mask=case.block_mask, block_size=case.block_size, heads=[bh])
-        oracle.backward(case.q, case.k, case.v, case.do, float(case.scale), causal=case.causal,
-                        key_len=case.key_len, block_mask=case.block_mask, block_size=case.block_size,
-                        heads=[bh])
+        kw = dict(causal=case.causal, key_len=case.key_len, block_mask=case.block_mask, block_size=case.block_size,
+                  heads=[bh])
+        O, LSE = oracle.forward(case.q, case.k, case.v, float(case.scale), **kw)
+        dQ, dK, dV = oracle.backward(case.q, case.k, case.v, case.do, float(case.scale), **kw)
         done.append(bh)
+        if gpu_instance is not None and len(parity) < 2:
+            el_ = time.perf_counter()
+            ref = {"o": O, "lse": LSE, "dq": dQ, "dk": dK, "dv": dV}
+            parity.append({"instance": list(bh), **_parity_of(gpu_instance(*bh), ref, bh)})
+            t0 += time.perf_counter() - el_  # (the comparison is not oracle time)
         if time.perf_counter() - t0 >= budget_s:
             break
     el = time.perf_counter() - t0
     flops = 14 * case.d * kept_pairs(case) * len(done) / (case.B * case.H)
-    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"float64 fwd+bwd of {len(done)} of {case.B * case.H} (batch, head) instances "
-                      f"at full N={case.N}, d={case.d}; {el:.1f} s wall"}
+    out = {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+           "sample": f"float64 fwd+bwd of {len(done)} of {case.B * case.H} (batch, head) instances "
+                     f"at full N={case.N}, d={case.d}; {el:.1f} s wall"}
+    return out, parity
 
 
 def cpu_table(budget_s: float):
@@ -247,26 +336,41 @@ def cpu_table(budget_s: float):
         print(json.dumps(row), flush=True)
 
 
-def standard_attention_step(q, k, v, do, scale: float, causal: bool):
+def standard_attention_step(q, k, v, do, scale: float, causal: bool, key_len=None, dropout_p: float = 0.0,
+                            keep=None):
     """The pages' baseline for the memory / runtime comparison, not part of the path:
     standard attention as separate framework ops that materialise S and P in HBM
     (FlashAttention reading notes, Background > Standard Attention Implementation),
     forward and the analytic backward, bf16 with float32 accumulation inside each
-    product. Every transposed operand is made contiguous before its product."""
+    product. Every transposed operand is made contiguous before its product.
+
+    key_len (int32 [B] on the device): keys j >= key_len[b] are masked. Dropout on P
+    (the notes' fused steps, Algorithm > Kernel Fusion) with drop probability dropout_p: the
+    keep bits are `keep` (bool [B, H, N, N]) when given, else drawn by torch; survivors are
+    scaled by 1 / (1 - dropout_p)."""
     import torch
+    n = q.shape[-2]
     kt = k.transpose(-1, -2).contiguous()
     s = torch.matmul(q, kt).mul_(scale)
     if causal:
-        n = q.shape[-2]
         s.masked_fill_(torch.ones(n, n, dtype=torch.bool, device=q.device).triu_(1), float("-inf"))
+    if key_len is not None:
+        cols = torch.arange(n, device=q.device)
+        s.masked_fill_((cols[None, :] >= key_len[:, None].long())[:, None, None, :], float("-inf"))
     p = torch.softmax(s, dim=-1)
     del s
-    o = torch.matmul(p, v)
-    pt = p.transpose(-1, -2).contiguous()
+    if keep is None and dropout_p > 0.0:
+        keep = torch.empty(p.shape, dtype=torch.bool, device=q.device).bernoulli_(1.0 - dropout_p)
+    ks = 1.0 / (1.0 - dropout_p)
+    pd = p if keep is None else p * keep * ks
+    o = torch.matmul(pd, v)
+    pt = pd.transpose(-1, -2).contiguous()
     dv = torch.matmul(pt, do)
-    del pt
+    del pt, pd  # (pd may be p itself: only the name goes)
     vt = v.transpose(-1, -2).contiguous()
     ds = torch.matmul(do, vt)  # dP, turned into dS = P (dP - D) in place
+    if keep is not None:
+        ds.mul_(keep).mul_(ks)
     dd = (do.float() * o.float()).sum(-1, keepdim=True).to(q.dtype)
     ds.sub_(dd).mul_(p)
     del p
@@ -277,24 +381,54 @@ def standard_attention_step(q, k, v, do, scale: float, causal: bool):
     return o, dq, dk, dv
 
 
-def memory_sweep(ns, B: int = 1, H: int = 16, d: int = 64, reps: int = 3):
-    """Peak device memory and time of one causal fwd + bwd step over N, for this
-    path and for standard attention (the pages' memory-footprint and runtime
-    benchmark, Experiments > 4.4; Theorem 1: extra memory O(N)). One JSON line per
-    N; memory is the peak above the four resident inputs."""
+SWEEP_SETTINGS = ("padding-dropout", "causal")
+
+
+def memory_sweep(ns, setting: str = "padding-dropout", B: int = 1, H: int = 16, d: int = 64, reps: int = 3,
+                 dropout_p: float = 0.1):
+    """Peak device memory and time of one fwd + bwd step over N, for this path and for
+    standard attention (the pages' memory-footprint and runtime benchmark, Experiments > 4.4;
+    Theorem 1: extra memory O(N)). One JSON line per N; memory is the peak above the four
+    resident inputs.
+
+    setting "padding-dropout" (the pages' benchmark: dropout and a padding mask): key padding
+    with a seeded key length uniform in [N/2, N], dropout p = 0.1; three lines: this path dense,
+    this path block-sparse (128 x 128 blocks, diagonal + symmetric p = 1/8, combined with the
+    padding), and standard attention. setting "causal": causal, no dropout; this path and
+    standard attention."""
     import numpy as np
     import torch
 
     import exact_attention_100_amd as fa
     import workloads
+    assert setting in SWEEP_SETTINGS, setting
     dev = torch.device("cuda:0")
+    # One small call of each line first, so that one-time library set-up (the matrix library's
+    # handles and workspace) is not charged to the first N.
+    w = torch.zeros((1, 1, 128, d), dtype=torch.bfloat16, device=dev)
+    standard_attention_step(w, w, w, w, 1.0, setting == "causal")
+    o_w, l_w = fa.fwd(w, w, w)
+    fa.bwd(w, w, w, o_w, w, l_w)
+    torch.cuda.synchronize()
+    del w, o_w, l_w
     for n in ns:
-        case = workloads.make_case(B, H, n, d, dtype=workloads.BF16, mask="causal", seed=100 + n.bit_length())
+        mask = "key_len" if setting == "padding-dropout" else "causal"
+        if setting == "padding-dropout" and n % 128 == 0:
+            mask = "key_len+block"
+        case = workloads.make_case(B, H, n, d, dtype=workloads.BF16, mask=mask, seed=100 + n.bit_length(),
+                                   key_len_range=(max(n // 2, 1), n), block_size=128 if "block" in mask else None,
+                                   block_p=0.125)
         t = {x: torch.from_numpy(case.bits(x).view(np.int16)).view(torch.bfloat16).to(dev)
              for x in ("q", "k", "v", "do")}
+        kl = None if case.key_len is None else torch.from_numpy(case.key_len).to(dev)
+        bm = None if case.block_mask is None else torch.from_numpy(case.block_mask).to(dev)
         sc = float(case.scale)
-        row = {"N": n, "B": B, "H": H, "d": d, "mask": "causal"}
-        for name in ("flash", "standard"):
+        causal = setting == "causal"
+        p = dropout_p if setting == "padding-dropout" else 0.0
+        row = {"N": n, "B": B, "H": H, "d": d, "setting": setting, "dropout_p": p,
+               "key_len": None if kl is None else case.key_len.tolist()}
+        lines = ["flash"] + (["flash_blocksparse"] if bm is not None else []) + ["standard"]
+        for name in lines:
             torch.cuda.synchronize()
             torch.cuda.empty_cache()
             base = torch.cuda.memory_allocated(dev)
@@ -302,9 +436,17 @@ def memory_sweep(ns, B: int = 1, H: int = 16, d: int = 64, reps: int = 3):
             try:
                 def step():
                     if name == "flash":
-                        o, lse = fa.fwd(t["q"], t["k"], t["v"], scale=sc, causal=True)
-                        return fa.bwd(t["q"], t["k"], t["v"], o, t["do"], lse, scale=sc, causal=True)
-                    return standard_attention_step(t["q"], t["k"], t["v"], t["do"], sc, True)
+                        o, lse = fa.fwd(t["q"], t["k"], t["v"], scale=sc, causal=causal, key_len=kl, dropout_p=p,
+                                        seed=7)
+                        return fa.bwd(t["q"], t["k"], t["v"], o, t["do"], lse, scale=sc, causal=causal,
+                                      key_len=kl, dropout_p=p, seed=7)
+                    if name == "flash_blocksparse":
+                        o, lse = fa.blocksparse_fwd(t["q"], t["k"], t["v"], bm, 128, scale=sc, key_len=kl,
+                                                    dropout_p=p, seed=7)
+                        return fa.blocksparse_bwd(t["q"], t["k"], t["v"], o, t["do"], lse, bm, 128, scale=sc,
+                                                  key_len=kl, dropout_p=p, seed=7)
+                    return standard_attention_step(t["q"], t["k"], t["v"], t["do"], sc, causal, key_len=kl,
+                                                   dropout_p=p)
                 step()
                 torch.cuda.synchronize()
                 peak = torch.cuda.max_memory_allocated(dev) - base
@@ -319,10 +461,12 @@ def memory_sweep(ns, B: int = 1, H: int = 16, d: int = 64, reps: int = 3):
                 row[name] = "out of memory"
             torch.cuda.synchronize()
             torch.cuda.empty_cache()
-        f, s = row["flash"], row["standard"]
-        if isinstance(f, dict) and isinstance(s, dict):
-            row["standard_over_flash"] = {"memory": round(s["peak_extra_bytes"] / f["peak_extra_bytes"], 2),
-                                          "time": round(s["ms_per_step"] / f["ms_per_step"], 2)}
+        s_ = row["standard"]
+        for name in lines[:-1]:
+            f = row[name]
+            if isinstance(f, dict) and isinstance(s_, dict):
+                row["standard_over_" + name] = {"memory": round(s_["peak_extra_bytes"] / f["peak_extra_bytes"], 2),
+                                                "time": round(s_["ms_per_step"] / f["ms_per_step"], 2)}
         print(json.dumps(row), flush=True)
         del t
 
@@ -345,15 +489,23 @@ def main():
     ap.add_argument("--digest-counters", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
                                                            "COPY_WRITE_DIR"),
                     help="print per-kernel HBM traffic from rocprofv3 --pmc csv runs")
+    ap.add_argument("--digest-sq", nargs=2, metavar=("P1_DIR", "P2_DIR"),
+                    help="print per-kernel SQ counter summaries from two rocprofv3 --pmc csv runs")
     ap.add_argument("--memory-sweep", nargs="*", type=int, metavar="N",
                     help="peak memory and time of this path and of standard attention over N "
-                         "(B=1, H=16, d=64, causal; default N = 1K .. 64K)")
+                         "(B=1, H=16, d=64; default N = 128 .. 64K)")
+    ap.add_argument("--sweep-setting", default="padding-dropout", choices=SWEEP_SETTINGS,
+                    help="the memory sweep's masks: key padding + dropout 0.1 (with a block-sparse line), "
+                         "or causal")
     args = ap.parse_args()
     if args.memory_sweep is not None:
-        memory_sweep(args.memory_sweep or [1 << e for e in range(10, 17)])
+        memory_sweep(args.memory_sweep or [1 << e for e in range(7, 17)], setting=args.sweep_setting)
         return
     if args.digest_counters:
         digest_counters(*args.digest_counters, workload=args.workload)
+        return
+    if args.digest_sq:
+        digest_sq(*args.digest_sq, workload=args.workload)
         return
     if args.calibrate_copy:
         calibrate_copy()
@@ -465,6 +617,17 @@ def main():
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": traffic_for(dom, args.workload)}
+    trec = _traffic_record(args.workload)
+    if roofline["traffic"] is not None:
+        roofline["traffic_source"] = counter_source("hbm_traffic", args.workload, trec)
+    hbm_step = step_traffic_for(args.workload)
+    if hbm_step is not None:
+        hbm_step = dict(hbm_step, source=counter_source("hbm_traffic", args.workload, trec))
+    sq = _sq_record(args.workload)
+    mfma_busy = None
+    if sq is not None:
+        mfma_busy = {k: v["mfma_busy"] for k, v in sq["kernels"].items()}
+        mfma_busy["source"] = counter_source("sq_counters", args.workload, sq)
 
     out = {
         "metric": "attention fwd+bwd TFLOP/s (bf16) and % of MI355X bf16 MFMA peak",
@@ -492,12 +655,22 @@ def main():
         "kernels": {k: {"mean_ms": round(v["mean_ms"], 4), "launches": v["launches"],
                         "share": round(v["share"], 4)} for k, v in kt.items()},
         "roofline": roofline,
-        "hbm_step": step_traffic_for(args.workload),
+        "mfma_busy": mfma_busy,
+        "hbm_step": hbm_step,
         "device_peak_bf16": {"value": device_peak_bf16_tflops(), "unit": "TFLOP/s",
                              "note": "reported peak engine clock x CUs x 4096 flop/clk/CU"},
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)
+        def gpu_instance(b, h):
+            # the outputs of the last timed step (every step writes the same values)
+            return {n: x[b, h].float().cpu().numpy().astype(np.float64)
+                    for n, x in (("o", o), ("lse", lse), ("dq", dq), ("dk", dk), ("dv", dv))}
+        torch.cuda.synchronize()
+        out["cpu_baseline"], parity = cpu_baseline(case, args.cpu_budget, gpu_instance if args.dropout == 0.0 else None)
+        if parity:
+            out["parity"] = {"reference": "float64 CPU oracle, computed in the cpu_baseline leg on the same inputs",
+                             "instances": parity,
+                             "within_tolerance": all(x["within_tolerance"] for x in parity)}
     print(json.dumps(out), flush=True)
 
 

@@ -187,9 +187,10 @@ def _mask_check(block_mask, q, block_size):
 
 
 def blocksparse_fwd(q, k, v, block_mask, block_size, scale=None, causal=False, key_len=None, out=None,
-                    lse=None, workspace=None):
+                    lse=None, workspace=None, dropout_p=0.0, seed=0, offset=0):
     """Block-sparse forward (zero blocks of block_mask skipped, combined by AND with the causal
-    and key-length masks); returns (O, LSE)."""
+    and key-length masks); returns (O, LSE). With dropout_p > 0, dropout on P as in fwd()
+    (fa_blocksparse_fwd_dropout)."""
     torch = _torch()
     d = _desc(q)
     _same_layout(q, k, v)
@@ -199,6 +200,13 @@ def blocksparse_fwd(q, k, v, block_mask, block_size, scale=None, causal=False, k
     B, H, N, _ = q.shape
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
     _lse_check(lse, q)
+    if dropout_p:
+        st = lib().fa_blocksparse_fwd_dropout(ctypes.byref(d), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                              _scale(scale, q.shape[-1]), int(bool(causal)), _ptr(kl),
+                                              block_mask.data_ptr(), int(block_size), float(dropout_p), int(seed),
+                                              int(offset), o.data_ptr(), lse.data_ptr(), _stream(q))
+        _check(st, "fa_blocksparse_fwd_dropout")
+        return o, lse
     need = int(lib().fa_blocksparse_workspace_bytes(ctypes.byref(d), int(block_size), 0))
     ws = None if (need == 0 and workspace is None) else _workspace(need, q, workspace)
     st = lib().fa_blocksparse_fwd(ctypes.byref(d), q.data_ptr(), k.data_ptr(), v.data_ptr(),
@@ -210,8 +218,9 @@ def blocksparse_fwd(q, k, v, block_mask, block_size, scale=None, causal=False, k
 
 
 def blocksparse_bwd(q, k, v, o, do, lse, block_mask, block_size, scale=None, causal=False, key_len=None,
-                    dq=None, dk=None, dv=None, workspace=None):
-    """Block-sparse backward; returns (dQ, dK, dV). Use the forward's mask, scale, causal, key_len."""
+                    dq=None, dk=None, dv=None, workspace=None, dropout_p=0.0, seed=0, offset=0):
+    """Block-sparse backward; returns (dQ, dK, dV). Use the forward's mask, scale, causal, key_len
+    and dropout (dropout_p, seed, offset)."""
     d = _desc(q)
     _same_layout(q, k, v, o, do)
     _lse_check(lse, q)
@@ -222,6 +231,15 @@ def blocksparse_bwd(q, k, v, o, do, lse, block_mask, block_size, scale=None, cau
     dv = _empty_like(q) if dv is None else dv
     need = int(lib().fa_blocksparse_workspace_bytes(ctypes.byref(d), int(block_size), 1))
     ws = _workspace(need, q, workspace)
+    if dropout_p:
+        st = lib().fa_blocksparse_bwd_dropout(ctypes.byref(d), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                              o.data_ptr(), do.data_ptr(), lse.data_ptr(), _scale(scale, q.shape[-1]),
+                                              int(bool(causal)), _ptr(kl), block_mask.data_ptr(), int(block_size),
+                                              float(dropout_p), int(seed), int(offset), dq.data_ptr(),
+                                              dk.data_ptr(), dv.data_ptr(), ws.data_ptr(),
+                                              ws.numel() * ws.element_size(), _stream(q))
+        _check(st, "fa_blocksparse_bwd_dropout")
+        return dq, dk, dv
     st = lib().fa_blocksparse_bwd(ctypes.byref(d), q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                                   do.data_ptr(), lse.data_ptr(), _scale(scale, q.shape[-1]),
                                   int(bool(causal)), _ptr(kl), block_mask.data_ptr(), int(block_size),

@@ -19,7 +19,8 @@ FA_BF16 = 0
 FA_F32 = 1
 
 EXPORTS = ("fa_fwd", "fa_bwd_workspace_bytes", "fa_bwd", "fa_fwd_dropout", "fa_bwd_dropout",
-           "fa_blocksparse_workspace_bytes", "fa_blocksparse_fwd", "fa_blocksparse_bwd", "fa_status_string",
+           "fa_blocksparse_workspace_bytes", "fa_blocksparse_fwd", "fa_blocksparse_bwd", "fa_blocksparse_fwd_dropout",
+           "fa_blocksparse_bwd_dropout", "fa_status_string",
            "fa_version", "fa_bwd_noalloc",
            "fa_timer_enable", "fa_timer_reset", "fa_timer_read")
 
@@ -72,6 +73,10 @@ def _load():
         "fa_blocksparse_bwd": (ctypes.c_int, [DESC, P, P, P, P, P, P, F32, ctypes.c_int, P, P, I32, P, P, P,
                                               P, SZ, P]),
         "fa_bwd_noalloc": (ctypes.c_int, [DESC, P, P, P, P, P, P, F32, ctypes.c_int, P, P, P, P, P]),
+        "fa_blocksparse_fwd_dropout": (ctypes.c_int, [DESC, P, P, P, F32, ctypes.c_int, P, P, I32, F32,
+                                                      ctypes.c_uint64, ctypes.c_uint32, P, P, P]),
+        "fa_blocksparse_bwd_dropout": (ctypes.c_int, [DESC, P, P, P, P, P, P, F32, ctypes.c_int, P, P, I32, F32,
+                                                      ctypes.c_uint64, ctypes.c_uint32, P, P, P, P, SZ, P]),
         "fa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "fa_version": (ctypes.c_int, []),
         "fa_timer_enable": (ctypes.c_int, [ctypes.c_int]),

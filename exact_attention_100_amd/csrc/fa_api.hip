@@ -411,3 +411,45 @@ extern "C" int fa_blocksparse_bwd(const fa_desc* desc, const void* Q, const void
   a.block_size = block_size;
   return hip_status(launch_bwd_bf16(a, static_cast<hipStream_t>(stream)));
 }
+
+extern "C" int fa_blocksparse_fwd_dropout(const fa_desc* desc, const void* Q, const void* K, const void* V,
+                                          float scale, int causal, const int32_t* key_len,
+                                          const uint8_t* block_mask, int32_t block_size, float dropout_p,
+                                          uint64_t seed, uint32_t offset, void* O, float* LSE, void* stream) {
+  int st = check_desc(desc);
+  if (st) return st;
+  if (desc->dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if ((st = check_scale(scale))) return st;
+  if ((st = check_ptrs({Q, K, V, O, LSE}))) return st;
+  if (!block_mask) return FA_ERR_INVALID;
+  if ((st = check_block(desc, block_size))) return st;
+  FwdArgs a = fwd_args(desc, Q, K, V, scale, causal != 0, key_len, O, LSE);
+  if ((st = make_dropout(dropout_p, seed, offset, a.dropout))) return st;
+  a.block_mask = block_mask;
+  a.nb = desc->N / block_size;
+  a.block_size = block_size;
+  return hip_status(launch_fwd_bf16(a, static_cast<hipStream_t>(stream)));
+}
+
+extern "C" int fa_blocksparse_bwd_dropout(const fa_desc* desc, const void* Q, const void* K, const void* V,
+                                          const void* O, const void* dO, const float* LSE, float scale, int causal,
+                                          const int32_t* key_len, const uint8_t* block_mask, int32_t block_size,
+                                          float dropout_p, uint64_t seed, uint32_t offset, void* dQ, void* dK,
+                                          void* dV, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_desc(desc);
+  if (st) return st;
+  if (desc->dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if ((st = check_scale(scale))) return st;
+  if ((st = check_ptrs({Q, K, V, O, dO, LSE, dQ, dK, dV}))) return st;
+  if (!block_mask) return FA_ERR_INVALID;
+  if ((st = check_block(desc, block_size))) return st;
+  if (!workspace || !aligned16(workspace) || workspace_bytes < bwd_ws_bytes(desc)) return FA_ERR_WORKSPACE;
+  BwdArgs a = bwd_args(desc, Q, K, V, O, dO, LSE, scale, causal != 0, key_len, dQ, dK, dV);
+  if ((st = make_dropout(dropout_p, seed, offset, a.dropout))) return st;
+  carve_bwd(desc, workspace, a);
+  a.block_mask = block_mask;
+  a.nb = desc->N / block_size;
+  a.block_size = block_size;
+  return hip_status(launch_bwd_bf16(a, static_cast<hipStream_t>(stream)));
+}
+

@@ -90,8 +90,8 @@ constexpr int kBwdBlock = 128;  // keys (dK/dV pass) or queries (dQ pass) per wo
 // VGPRs, which keeps the d = 128 kernel within 256 registers (two waves per SIMD).
 // SMASK: a block-sparse launch that also applies the causal / key-length
 // element masks (without it, sparse tiles are never masked).
-// DROP: dropout on P (dense launches), the keep bits regenerated from the same
-// counters as the forward: dV takes P o Z / (1 - p) and dP is masked and scaled
+// DROP: dropout on P (dense and block-sparse launches), the keep bits regenerated
+// from the same counters as the forward: dV takes P o Z / (1 - p) and dP is masked and scaled
 // the same way before dS = P (dP - D).
 template <int D, int BRQ, bool SPARSE, bool VLDS, bool SMASK = false, bool DROP = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FA_BWD_WAVES_PER_EU)))
@@ -933,7 +933,7 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s) {
   p.n_blocks = (a.N + kBwdBlock - 1) / kBwdBlock;
   const bool sparse = a.block_mask != nullptr;
   const bool smask = a.causal || a.key_len != nullptr;
-  const bool drop = a.dropout.p8 != 0 && !sparse;
+  const bool drop = a.dropout.p8 != 0;
   p.drop = a.dropout;
   const dim3 block(256);
 
@@ -942,14 +942,18 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)(a.B * a.H * p.n_blocks));
   // The dQ pass first: it also writes each row's D and lse2, which the dK/dV
   // pass reads for every query tile it visits.
+  // Block-sparse with dropout always takes the element-masked variant (with neither causal
+  // nor key_len no tile needs masking).
   timer_begin("fa_bwd_dq", s);
   if (a.d == 128) {
-    if (drop) bwd_dq_kernel<128, FA_BWD_TILE_K_DROP_D128, false, false, true><<<grid, block, 0, s>>>(p);
+    if (drop && sparse) bwd_dq_kernel<128, FA_BWD_TILE_K_DROP_D128, true, true, true><<<grid, block, 0, s>>>(p);
+    else if (drop) bwd_dq_kernel<128, FA_BWD_TILE_K_DROP_D128, false, false, true><<<grid, block, 0, s>>>(p);
     else if (sparse && smask) bwd_dq_kernel<128, TK128, true, true><<<grid, block, 0, s>>>(p);
     else if (sparse) bwd_dq_kernel<128, TK128, true><<<grid, block, 0, s>>>(p);
     else bwd_dq_kernel<128, TK128, false><<<grid, block, 0, s>>>(p);
   } else {
-    if (drop) bwd_dq_kernel<64, TK64, false, false, true><<<grid, block, 0, s>>>(p);
+    if (drop && sparse) bwd_dq_kernel<64, TK64, true, true, true><<<grid, block, 0, s>>>(p);
+    else if (drop) bwd_dq_kernel<64, TK64, false, false, true><<<grid, block, 0, s>>>(p);
     else if (sparse && smask) bwd_dq_kernel<64, TK64, true, true><<<grid, block, 0, s>>>(p);
     else if (sparse) bwd_dq_kernel<64, TK64, true><<<grid, block, 0, s>>>(p);
     else bwd_dq_kernel<64, TK64, false><<<grid, block, 0, s>>>(p);
@@ -960,12 +964,14 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s) {
 
   timer_begin("fa_bwd_dkdv", s);
   if (a.d == 128) {
-    if (drop) bwd_dkdv_kernel<128, TQ128, false, true, false, true><<<grid, block, 0, s>>>(p);
+    if (drop && sparse) bwd_dkdv_kernel<128, TQ128, true, true, true, true><<<grid, block, 0, s>>>(p);
+    else if (drop) bwd_dkdv_kernel<128, TQ128, false, true, false, true><<<grid, block, 0, s>>>(p);
     else if (sparse && smask) bwd_dkdv_kernel<128, TQ128, true, true, true><<<grid, block, 0, s>>>(p);
     else if (sparse) bwd_dkdv_kernel<128, TQ128, true, true><<<grid, block, 0, s>>>(p);
     else bwd_dkdv_kernel<128, TQ128, false, true><<<grid, block, 0, s>>>(p);
   } else {
-    if (drop) bwd_dkdv_kernel<64, TQ64, false, false, false, true><<<grid, block, 0, s>>>(p);
+    if (drop && sparse) bwd_dkdv_kernel<64, TQ64, true, false, true, true><<<grid, block, 0, s>>>(p);
+    else if (drop) bwd_dkdv_kernel<64, TQ64, false, false, false, true><<<grid, block, 0, s>>>(p);
     else if (sparse && smask) bwd_dkdv_kernel<64, TQ64, true, false, true><<<grid, block, 0, s>>>(p);
     else if (sparse) bwd_dkdv_kernel<64, TQ64, true, false><<<grid, block, 0, s>>>(p);
     else bwd_dkdv_kernel<64, TQ64, false, false><<<grid, block, 0, s>>>(p);

@@ -198,8 +198,9 @@ __device__ __forceinline__ float softmax_tile_bf16(f32x16 (&s)[NKB], float c, fl
 
 // SMASK: a block-sparse launch that also applies the causal / key-length
 // element masks (without it, sparse tiles are never masked). DROP: dropout on P
-// (dense launches): dropped entries of the packed bf16 probabilities are zeroed
-// after their row sum is taken, and O is scaled by 1 / (1 - p) at the end.
+// (dense and block-sparse launches): dropped entries of the packed bf16
+// probabilities are zeroed after their row sums are taken, and O is scaled by
+// 1 / (1 - p) at the end.
 template <int D, int BC, bool SPARSE, bool SMASK = false, bool DROP = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FA_FWD_WAVES_PER_EU)))
 void fwd_bf16_kernel(FwdKParams p) {
@@ -623,7 +624,11 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s) {
   const bool smask = a.causal || a.key_len != nullptr;
   timer_begin("fa_fwd_bf16", s);
   constexpr int BC128 = FA_FWD_BC_D128, BC64 = FA_FWD_BC_D64, BCS64 = FA_FWD_BC_SPARSE_D64;
-  if (a.dropout.p8 && !sparse) {
+  if (a.dropout.p8 && sparse) {
+    // (the element masks are applied per tile as needed; with neither causal nor key_len no tile needs them)
+    if (a.d == 128) fwd_bf16_kernel<128, BC128, true, true, true><<<grid, block, 0, s>>>(p);
+    else fwd_bf16_kernel<64, BCS64, true, true, true><<<grid, block, 0, s>>>(p);
+  } else if (a.dropout.p8) {
     if (a.d == 128) fwd_bf16_kernel<128, BC128, false, false, true><<<grid, block, 0, s>>>(p);
     else fwd_bf16_kernel<64, BC64, false, false, true><<<grid, block, 0, s>>>(p);
   } else if (a.d == 128) {

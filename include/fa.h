@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define FA_VERSION 103
+#define FA_VERSION 104
 
 enum fa_status {
   FA_OK = 0,
@@ -147,7 +147,8 @@ int fa_blocksparse_bwd(const fa_desc* desc, const void* Q, const void* K, const 
  * p8 = round(256 dropout_p); the drop probability applied is p8 / 256. LSE is
  * that of the softmax before dropout. dropout_p must lie in [0, 1) (else
  * FA_ERR_INVALID); p8 = 0 is fa_fwd. bf16 only when p8 > 0 (else
- * FA_ERR_UNSUPPORTED). Dense, causal and key_len masks; not block-sparse. */
+ * FA_ERR_UNSUPPORTED). Dense, causal and key_len masks (block-sparse:
+ * fa_blocksparse_fwd_dropout). */
 int fa_fwd_dropout(const fa_desc* desc, const void* Q, const void* K, const void* V, float scale,
                    int causal, const int32_t* key_len, float dropout_p, uint64_t seed,
                    uint32_t offset, void* O, float* LSE, void* stream);
@@ -177,6 +178,25 @@ int fa_bwd_dropout(const fa_desc* desc, const void* Q, const void* K, const void
 int fa_bwd_noalloc(const fa_desc* desc, const void* Q, const void* K, const void* V, const void* O,
                    const void* dO, const float* LSE, float scale, int causal, const int32_t* key_len,
                    void* dQ, void* dK, void* dV, void* stream);
+
+/* Block-sparse forward with dropout on P: fa_blocksparse_fwd (same mask,
+ * causal and key_len semantics and requirements) with the dropout of
+ * fa_fwd_dropout (same keep bits, scaling and LSE; reading notes, §Algorithm ›
+ * Kernel Fusion: masking and dropout in the one fused kernel; §Experiments ›
+ * 4.4 runs block-sparse attention with dropout). dropout_p in [0, 1) (else
+ * FA_ERR_INVALID); bf16 only. */
+int fa_blocksparse_fwd_dropout(const fa_desc* desc, const void* Q, const void* K, const void* V,
+                               float scale, int causal, const int32_t* key_len,
+                               const uint8_t* block_mask, int32_t block_size, float dropout_p,
+                               uint64_t seed, uint32_t offset, void* O, float* LSE, void* stream);
+
+/* Backward of fa_blocksparse_fwd_dropout: needs the same mask, scale, causal,
+ * key_len and (dropout_p, seed, offset). Workspace as fa_blocksparse_bwd. */
+int fa_blocksparse_bwd_dropout(const fa_desc* desc, const void* Q, const void* K, const void* V,
+                               const void* O, const void* dO, const float* LSE, float scale, int causal,
+                               const int32_t* key_len, const uint8_t* block_mask, int32_t block_size,
+                               float dropout_p, uint64_t seed, uint32_t offset, void* dQ, void* dK,
+                               void* dV, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static, human-readable name of a status code. */
 const char* fa_status_string(int status);

@@ -26,7 +26,8 @@ def _header_functions():
 def test_header_declares_the_expected_entry_points():
     names = _header_functions()
     for n in ("fa_fwd", "fa_bwd", "fa_fwd_dropout", "fa_bwd_dropout", "fa_blocksparse_fwd",
-              "fa_blocksparse_bwd", "fa_bwd_workspace_bytes", "fa_blocksparse_workspace_bytes",
+              "fa_blocksparse_bwd", "fa_blocksparse_fwd_dropout", "fa_blocksparse_bwd_dropout",
+              "fa_bwd_workspace_bytes", "fa_blocksparse_workspace_bytes", "fa_bwd_noalloc",
               "fa_status_string", "fa_version"):
         assert n in names
 
@@ -38,7 +39,7 @@ def test_library_exports_every_header_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.fa_version() == 103
+    assert lib.fa_version() == 104
     for code in (0, -1, -2, -3, -4, -5):
         assert lib.fa_status_string(code)
     assert b"unknown" in lib.fa_status_string(7)
@@ -79,6 +80,18 @@ def test_argument_errors_before_any_launch(lib):
     assert lib.fa_fwd_dropout(ref(_desc(dtype=1)), A, A, A, 0.1, 0, None, 0.1, 1, 0, A, A, None) == -2
     assert lib.fa_bwd_dropout(ref(_desc(dtype=1)), A, A, A, A, A, A, 0.1, 0, None, 0.1, 1, 0, A, A, A, A,
                               1 << 30, None) == -2
+    # block-sparse dropout: the block-size, mask, probability, dtype and workspace checks
+    for p in (-0.1, 1.0, float("nan")):
+        assert lib.fa_blocksparse_fwd_dropout(ref(d), A, A, A, 0.1, 0, None, A, 128, p, 1, 0, A, A, None) == -1
+        assert lib.fa_blocksparse_bwd_dropout(ref(d), A, A, A, A, A, A, 0.1, 0, None, A, 128, p, 1, 0, A, A, A, A,
+                                              1 << 30, None) == -1
+    assert lib.fa_blocksparse_fwd_dropout(ref(d), A, A, A, 0.1, 0, None, None, 128, 0.1, 1, 0, A, A, None) == -1
+    assert lib.fa_blocksparse_fwd_dropout(ref(d), A, A, A, 0.1, 0, None, A, 100, 0.1, 1, 0, A, A, None) == -1
+    assert lib.fa_blocksparse_fwd_dropout(ref(_desc(dtype=1)), A, A, A, 0.1, 0, None, A, 128, 0.1, 1, 0, A, A,
+                                          None) == -2
+    need_bs = lib.fa_bwd_workspace_bytes(ref(d))
+    assert lib.fa_blocksparse_bwd_dropout(ref(d), A, A, A, A, A, A, 0.1, 0, None, A, 128, 0.1, 1, 0, A, A, A, A,
+                                          need_bs - 1, None) == -3
     # block-sparse: block size must be a multiple of 128 that divides N
     for bs in (64, 100, 192, 512):
         assert lib.fa_blocksparse_fwd(ref(d), A, A, A, 0.1, 0, None, A, bs, A, A, A, 1 << 30, None) == -1
