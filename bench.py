@@ -120,10 +120,16 @@ def counter_source(kind: str, workload: str, rec) -> str:
             f"same command on one MI355X (not this run's box), kernel sources_hash {rec['sources_hash']}")
 
 
-def digest_sq(p1: str, p2: str, workload: str):
-    """Per-kernel SQ counter summary from two rocprofv3 --pmc csv runs (the two counter sets of the
-    profile's header): the matrix cores' busy fraction, where the waves' time goes, and instructions
-    per MFMA. Prints the text and the JSON that bench.py reads."""
+# The two SQ counter sets (one rocprofv3 --pmc run each: at most 8 SQ and 2 GRBM counters per run).
+SQ_SETS = (["SQ_WAVE_CYCLES", "SQ_BUSY_CU_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY",
+            "SQ_ACTIVE_INST_ANY", "SQ_WAIT_INST_LDS", "SQ_LDS_BANK_CONFLICT"],
+           ["SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_INSTS_SALU", "SQ_INSTS_VMEM", "SQ_ACTIVE_INST_VALU",
+            "SQ_ACTIVE_INST_LDS", "GRBM_GUI_ACTIVE"])
+
+
+def sq_digest(p1: str, p2: str, workload: str):
+    """Per-kernel SQ counter summary from two rocprofv3 --pmc csv runs (SQ_SETS): the matrix cores'
+    busy fraction, where the waves' time goes, and instructions per MFMA. Returns (record, text)."""
     import csv
     import glob
     import re
@@ -136,6 +142,7 @@ def digest_sq(p1: str, p2: str, workload: str):
                     k = k.replace("(fa::FwdKParams)", "").replace("(fa::BwdKParams)", "")
                     vals.setdefault(k, {}).setdefault(row["Counter_Name"], []).append(float(row["Counter_Value"]))
     out = {"workload": workload, "sources_hash": sources_hash(), "kernels": {}}
+    lines = []
     for k, cs in vals.items():
         name = next((v for frag, v in KERNEL_NAMES.items() if frag in k), None)
         if name is None:
@@ -148,13 +155,19 @@ def digest_sq(p1: str, p2: str, workload: str):
                "valu_per_mfma": round((m["SQ_INSTS_VALU"] - mf) / mf, 2), "lds_per_mfma": round(m["SQ_INSTS_LDS"] / mf, 2),
                "salu_per_mfma": round(m["SQ_INSTS_SALU"] / mf, 2), "lds_bank_conflicts": m["SQ_LDS_BANK_CONFLICT"]}
         out["kernels"][name] = rec
-        print(k)
-        print("  " + "  ".join(f"{c}={m[c]:.4g}" for c in sorted(m)))
-        print(f"  mfma_busy {busy:.3f}; wave time: issuing {rec['issuing']:.2f}, waiting {rec['waiting']:.2f}, "
-              f"issue-stalled {rec['issue_stalled']:.2f}; per MFMA: {rec['valu_per_mfma']:.2f} other VALU, "
-              f"{rec['lds_per_mfma']:.2f} LDS, {rec['salu_per_mfma']:.2f} SALU; LDS bank conflicts "
-              f"{m['SQ_LDS_BANK_CONFLICT']:.0f}\n", flush=True)
-    print(json.dumps(out, indent=1), flush=True)
+        lines += [k, "  " + "  ".join(f"{c}={m[c]:.4g}" for c in sorted(m)),
+                  f"  mfma_busy {busy:.3f}; wave time: issuing {rec['issuing']:.2f}, waiting {rec['waiting']:.2f}, "
+                  f"issue-stalled {rec['issue_stalled']:.2f}; per MFMA: {rec['valu_per_mfma']:.2f} other VALU, "
+                  f"{rec['lds_per_mfma']:.2f} LDS, {rec['salu_per_mfma']:.2f} SALU; LDS bank conflicts "
+                  f"{m['SQ_LDS_BANK_CONFLICT']:.0f}", ""]
+    return out, "\n".join(lines)
+
+
+def digest_sq(p1: str, p2: str, workload: str):
+    """Prints sq_digest's text and the JSON that bench.py reads from profiles/."""
+    rec, text = sq_digest(p1, p2, workload)
+    print(text, flush=True)
+    print(json.dumps(rec, indent=1), flush=True)
 
 
 def step_traffic_for(workload: str):
@@ -195,11 +208,12 @@ def _counter_means(d: str, counter: str):
     return {k: sum(v) / len(v) for k, v in vals.items()}
 
 
-def digest_counters(fetch_dir: str, write_dir: str, copy_fetch_dir: str, copy_write_dir: str, workload: str):
+def traffic_digest(fetch_dir: str, write_dir: str, copy_fetch_dir: str, copy_write_dir: str, workload: str):
     """Per-kernel HBM bytes per launch from FETCH_SIZE / WRITE_SIZE (KiB) runs, each scaled by what the
-    counter reads for the calibration copy of known size. Prints the JSON that bench.py reads."""
+    counter reads for the calibration copy of known size; the step's sum against the algorithmic bytes and
+    the standard-attention byte model."""
     import workloads
-    case = workloads.make_config(workload)
+    c = workloads.CONFIGS[workload]
     cf, cw = _counter_means(copy_fetch_dir, "FETCH_SIZE"), _counter_means(copy_write_dir, "WRITE_SIZE")
     # the calibration copy is the dispatch with the largest traffic in its run
     copy_bytes = 1 << 30
@@ -207,7 +221,7 @@ def digest_counters(fetch_dir: str, write_dir: str, copy_fetch_dir: str, copy_wr
     kw = copy_bytes / (max(cw.values()) * 1024.0)
     fetch, write = _counter_means(fetch_dir, "FETCH_SIZE"), _counter_means(write_dir, "WRITE_SIZE")
     e = 2
-    B, H, N, d = case.B, case.H, case.N, case.d
+    B, H, N, d = c["B"], c["H"], c["N"], c["d"]
     rows = B * H * N
     algo = {"fa_fwd_bf16": 4 * rows * d * e + 4 * rows, "fa_bwd_dkdv": 6 * rows * d * e + 8 * rows,
             "fa_bwd_dq": 6 * rows * d * e + 12 * rows}
@@ -233,7 +247,77 @@ def digest_counters(fetch_dir: str, write_dir: str, copy_fetch_dir: str, copy_wr
            "step": {"hbm_bytes_measured": round(measured), "algorithmic_bytes": algorithmic,
                     "standard_attention_model_bytes": standard,
                     "standard_over_measured": round(standard / measured, 2)}}
-    print(json.dumps(out, indent=1), flush=True)
+    return out
+
+
+def digest_counters(fetch_dir: str, write_dir: str, copy_fetch_dir: str, copy_write_dir: str, workload: str):
+    """Prints traffic_digest's JSON (the form bench.py reads from profiles/)."""
+    print(json.dumps(traffic_digest(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, workload), indent=1),
+          flush=True)
+
+
+def _rocprofv3():
+    import shutil
+    for cand in ("/opt/rocm/bin/rocprofv3", shutil.which("rocprofv3")):
+        if cand and os.path.exists(cand):
+            return cand
+    return None
+
+
+def _profile_child(prof: str, counters, out_dir: str, args, timeout_s: float) -> bool:
+    """One rocprofv3 --pmc pass (its own child process, killed with its process group past
+    timeout_s) over `python3 bench.py <args>`; True if it left a counter csv. rocprofv3 can end
+    with a segmentation fault after the program has finished: the csv decides, not the status."""
+    import glob
+    import signal
+    import subprocess
+    cmd = [prof, "--pmc", *counters, "-d", out_dir, "-o", "p", "--output-format", "csv", "--",
+           sys.executable, os.path.join(ROOT, "bench.py"), *args]
+    env = dict(os.environ, TMPDIR=os.environ.get("TMPDIR", "/tmp"))
+    p = subprocess.Popen(cmd, cwd=ROOT, env=env, stdout=subprocess.DEVNULL, stderr=subprocess.DEVNULL,
+                         start_new_session=True)
+    try:
+        p.wait(timeout=timeout_s)
+    except subprocess.TimeoutExpired:
+        os.killpg(p.pid, signal.SIGKILL)
+        p.wait()
+        return False
+    return bool(glob.glob(os.path.join(out_dir, "**", "*counter_collection.csv"), recursive=True))
+
+
+def measure_counters(workload: str, lib, timeout_s: float = 240.0):
+    """HBM traffic and SQ counters of this workload measured now, on this machine: rocprofv3 --pmc passes
+    (FETCH_SIZE, WRITE_SIZE, the two SQ sets, and FETCH_SIZE / WRITE_SIZE of the 1 GiB calibration copy),
+    each over a 2-step run of this bench command in a child process. Returns (traffic, sq); either is
+    None if its passes failed."""
+    import tempfile
+    prof = _rocprofv3()
+    if prof is None:
+        return None, None
+    base = ["--workload", workload, "--steps", "2", "--warmup", "1", "--no-cpu-baseline", "--counters", "off"]
+    if lib:
+        base += ["--lib", lib]
+    tmp = tempfile.mkdtemp(prefix="fa_counters_")
+    d = {k: os.path.join(tmp, k) for k in ("fetch", "write", "cfetch", "cwrite", "sq1", "sq2")}
+    ok = {}
+    for key, counters, args in (("fetch", ["FETCH_SIZE"], base), ("write", ["WRITE_SIZE"], base),
+                                ("cfetch", ["FETCH_SIZE"], ["--calibrate-copy"]),
+                                ("cwrite", ["WRITE_SIZE"], ["--calibrate-copy"]),
+                                ("sq1", SQ_SETS[0], base), ("sq2", SQ_SETS[1], base)):
+        print(f"bench.py: counter pass {key}", file=sys.stderr, flush=True)
+        ok[key] = _profile_child(prof, counters, d[key], args, timeout_s)
+    traffic = sq = None
+    try:
+        if all(ok[k] for k in ("fetch", "write", "cfetch", "cwrite")):
+            traffic = traffic_digest(d["fetch"], d["write"], d["cfetch"], d["cwrite"], workload)
+    except (KeyError, ValueError, ZeroDivisionError):
+        traffic = None
+    try:
+        if ok["sq1"] and ok["sq2"]:
+            sq = sq_digest(d["sq1"], d["sq2"], workload)[0]
+    except (KeyError, ValueError, ZeroDivisionError):
+        sq = None
+    return traffic, sq
 
 
 def _parity_of(gpu, ref, bh):
@@ -489,6 +573,9 @@ def main():
     ap.add_argument("--digest-counters", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
                                                            "COPY_WRITE_DIR"),
                     help="print per-kernel HBM traffic from rocprofv3 --pmc csv runs")
+    ap.add_argument("--counters", default="auto", choices=("auto", "off"),
+                    help="auto: measure HBM traffic and SQ counters of the benched workload in rocprofv3 child "
+                         "runs on this box (falls back to the committed digests if that fails)")
     ap.add_argument("--digest-sq", nargs=2, metavar=("P1_DIR", "P2_DIR"),
                     help="print per-kernel SQ counter summaries from two rocprofv3 --pmc csv runs")
     ap.add_argument("--memory-sweep", nargs="*", type=int, metavar="N",
@@ -617,17 +704,30 @@ def main():
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": traffic_for(dom, args.workload)}
-    trec = _traffic_record(args.workload)
-    if roofline["traffic"] is not None:
-        roofline["traffic_source"] = counter_source("hbm_traffic", args.workload, trec)
-    hbm_step = step_traffic_for(args.workload)
-    if hbm_step is not None:
-        hbm_step = dict(hbm_step, source=counter_source("hbm_traffic", args.workload, trec))
-    sq = _sq_record(args.workload)
+    live_traffic = live_sq = None
+    if args.counters == "auto" and args.dropout == 0.0:
+        live_traffic, live_sq = measure_counters(args.workload, args.lib)
+    here = ("this run: rocprofv3 --pmc passes over `bench.py --workload {w} --steps 2` started by this bench "
+            "as child processes on this box ({what})")
+    if live_traffic is not None and dom in live_traffic["kernels"]:
+        roofline["traffic"] = live_traffic["kernels"][dom]["hbm_bytes_per_launch"]
+        roofline["traffic_source"] = here.format(w=args.workload, what="FETCH_SIZE, WRITE_SIZE, each scaled by "
+                                                 "the same counter on a 1 GiB copy")
+        hbm_step = dict(live_traffic["step"], source=roofline["traffic_source"])
+    else:
+        trec = _traffic_record(args.workload)
+        if roofline["traffic"] is not None:
+            roofline["traffic_source"] = counter_source("hbm_traffic", args.workload, trec)
+        hbm_step = step_traffic_for(args.workload)
+        if hbm_step is not None:
+            hbm_step = dict(hbm_step, source=counter_source("hbm_traffic", args.workload, trec))
+    sq = live_sq if live_sq is not None else _sq_record(args.workload)
     mfma_busy = None
     if sq is not None:
         mfma_busy = {k: v["mfma_busy"] for k, v in sq["kernels"].items()}
-        mfma_busy["source"] = counter_source("sq_counters", args.workload, sq)
+        mfma_busy["source"] = (here.format(w=args.workload, what="SQ_VALU_MFMA_BUSY_CYCLES / 1024 over "
+                                           "GRBM_GUI_ACTIVE / 8") if live_sq is not None
+                               else counter_source("sq_counters", args.workload, sq))
 
     out = {
         "metric": "attention fwd+bwd TFLOP/s (bf16) and % of MI355X bf16 MFMA peak",
