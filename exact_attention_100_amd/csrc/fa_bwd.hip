@@ -559,6 +559,10 @@ void bwd_dkdv_kernel(BwdKParams p) {
 #ifndef FA_BWD_TILE_K_D64
 #define FA_BWD_TILE_K_D64 64
 #endif
+// Dense d = 128 without dropout: the dQ pass as two wave groups (bwd_dq_pp_kernel).
+#ifndef FA_BWD_DQ_PINGPONG
+#define FA_BWD_DQ_PINGPONG 1
+#endif
 
 // Per key tile of BC keys (double-buffered in LDS by direct copies), each wave,
 // for its 32 queries (one query per lane column, as in the forward):
@@ -901,6 +905,258 @@ void bwd_dq_kernel(BwdKParams p) {
   }
 }
 
+// --------------------------------------------------------------- dQ, two wave groups
+
+// The dQ pass with the products and the element work in different waves at any one
+// time (the scheme of the two-group forward): 8 waves own 256 query rows, waves w and
+// w + 4 share a SIMD and form two groups that run half a key tile apart, separated by
+// workgroup barriers. Wave (group gr, index wg) owns the 32 rows q0 + 64 wg + 32 gr ..
+//   product phase t:  dQ^T += K_{t-1}^T dS^T(t - 1), S^T(t) = K_t Q^T, dP^T(t) = V_t dO^T;
+//   element phase t:  mask, P = 2^(c S - lse2), dS = P (dP - D), bf16 packing of dS.
+// K tiles are kept for three tiles (tile t - 1 is read by the dQ products of phase t),
+// V tiles for two; group 0 copies tile t + 1's K and V during its product phase t and
+// waits for them at the end of its element phase t (splitting the copies between the
+// groups, with V kept for three tiles, measured 1% slower).
+constexpr int kBwdRowsPP = 256;
+#ifndef FA_BWD_DQ_PP_AHEAD
+#define FA_BWD_DQ_PP_AHEAD 3
+#endif
+
+template <int D, int BC>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
+void bwd_dq_pp_kernel(BwdKParams p) {
+  constexpr int NKB = BC / 32;
+  constexpr int NDB = D / 32;
+  constexpr int NKK = D / 16;
+  constexpr int TILE = BC * D;
+  constexpr int NS = NKK * NKB;          // S products (as many dP products)
+  constexpr int NQM = (BC / 16) * NDB;   // dQ products
+  constexpr int NCP = BC * D / 8 / (64 * 4);  // copies per wave of group 0 per tile (K or V)
+  __shared__ __attribute__((aligned(16))) bf16 sT[5 * TILE];  // [K0 | K1 | K2 | V0 | V1]
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = uniform_wave_id();
+  const int gr = wave >> 2, wg = wave & 3;
+  const int l32 = lane & 31, g = lane >> 5;
+  const int N = p.N;
+  int inst, rank;
+  schedule_tile(blockIdx.x, p.B * p.H, p.n_blocks, inst, rank);
+  const int qb = p.causal ? (p.n_blocks - 1 - rank) : rank;  // heaviest causal rows first
+  const int b = inst / p.H, h = inst - b * p.H;
+  const int64_t base = (int64_t)b * p.sb + (int64_t)h * p.sh;
+  const bf16* Qh = p.q + base;
+  const bf16* Kh = p.k + base;
+  const bf16* Vh = p.v + base;
+  const bf16* dOh = p.dout + base;
+  const int q0 = qb * kBwdRowsPP;
+  const int wrow0 = q0 + 64 * wg + 32 * gr;
+  const int qrow = wrow0 + l32;
+  const int qc = min(qrow, N - 1);
+  const int64_t rowbase = (int64_t)inst * N;
+  int kv_len = N;
+  if (p.key_len) kv_len = min(max(p.key_len[b], 0), N);
+  int kv_end = kv_len;
+  if (p.causal) kv_end = min(kv_end, q0 + kBwdRowsPP);
+  const int nt = kv_end > 0 ? (kv_end + BC - 1) / BC : 0;
+
+  // This lane's rows of Q and dO as B operands (dims [16 kk + 8 g, +8)).
+  bf16x8 qf[NKK], df[NKK];
+  const int64_t qoff = (int64_t)qc * p.sn + 8 * g;
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) {
+    qf[kk] = *reinterpret_cast<const bf16x8*>(Qh + qoff + 16 * kk);
+    df[kk] = *reinterpret_cast<const bf16x8*>(dOh + qoff + 16 * kk);
+  }
+  f32x16 dqacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dqacc[db][r] = 0.f;
+
+  TileCopy<BC, D, 4> cp;
+  cp.init(wg, lane, p.sn);
+  TileAddr<D> ta;
+  {
+    TileOffsets<D> to;
+    to.init(lane);
+    ta.init(to, lds_address(sT));
+  }
+  auto kv0_of = [&](int t) { return min(t, nt - 1) * BC; };
+  auto kbuf = [](int j) { return 2 * TILE * j; };        // byte offsets in sT
+  auto vbuf = [](int j) { return 2 * TILE * (3 + j); };
+  if (nt > 0 && gr == 0) {
+    cp.issue(sT + kbuf(0) / 2, Kh, p.sn, kv0_of(0), N);
+    cp.issue(sT + vbuf(0) / 2, Vh, p.sn, kv0_of(0), N);
+  }
+
+  // D = sum_i dO_i O_i (this lane's half of the dims, then its partner's) and
+  // lse2 = LSE log2(e) (+inf for a row with no key), formed while the first copies are
+  // in flight and written to the workspace for the dK/dV pass.
+  float d_half = 0.f;
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) {
+    const bf16x8 ov = *reinterpret_cast<const bf16x8*>(p.o + base + qoff + 16 * kk);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) d_half = fmaf((float)ov[i], (float)df[kk][i], d_half);
+  }
+  const float d_q = pair_sum(d_half);
+  const float lse_q = p.lse[rowbase + qc];
+  const float lse2_q = (lse_q == kNegInf) ? kPosInf : lse_q * kLog2e;
+  if (qrow < N && g == 0) {
+    p.delta[rowbase + qrow] = d_q;
+    p.lse2[rowbase + qrow] = lse2_q;
+  }
+
+  f32x16 sacc[NKB], dpacc[NKB];
+  bf16x8 dsb[2 * NKB];
+
+  // Product phase: (DQ) dQ^T += K_{t-1}^T dS^T(t - 1) from the K buffer at kp, then
+  // S^T(t) and dP^T(t) from the K / V buffers at kb / vb. LDS operands are inline-
+  // assembly reads issued AH products ahead and waited for exactly.
+  auto products = [&](int kp, int kb, int vb, auto dq_flag) __attribute__((always_inline)) {
+    constexpr bool DQ = decltype(dq_flag)::value;
+    constexpr int NQ = DQ ? NQM : 0;
+    constexpr int NM = NQ + 2 * NS, AH = FA_BWD_DQ_PP_AHEAD;
+    bf16x8 ra[AH + 1];
+    int ia[AH + 1];
+    int nrd = 0;
+    auto fetch = [&](int m) __attribute__((always_inline)) {
+      const int sl = m % (AH + 1);
+      if (m < NQ) {
+        ra[sl] = ta.read_tr(kp, m / NDB, m % NDB);
+        nrd += 2;
+      } else if (m < NQ + NS) {
+        const int j = m - NQ;
+        ra[sl] = ta.read_row(kb, j / NKK, j % NKK);
+        nrd += 1;
+      } else {
+        const int j = m - NQ - NS;
+        ra[sl] = ta.read_row(vb, j / NKK, j % NKK);
+        nrd += 1;
+      }
+      ia[sl] = nrd - 1;
+    };
+#pragma unroll
+    for (int m = 0; m < AH && m < NM; ++m) fetch(m);
+    static_for<NM>([&](auto mc) __attribute__((always_inline)) {
+      constexpr int m = decltype(mc)::value;
+      if (m + AH < NM) fetch(m + AH);
+      lds_wait(nrd - 1 - ia[m % (AH + 1)]);
+      __builtin_amdgcn_sched_barrier(0);
+      const bf16x8 a = ra[m % (AH + 1)];
+      if constexpr (m < NQ) {
+        dqacc[m % NDB] = mfma_bf16(a, dsb[m / NDB], dqacc[m % NDB]);
+      } else if constexpr (m < NQ + NS) {
+        constexpr int j = m - NQ;
+        sacc[j / NKK] = mfma_bf16(a, qf[j % NKK], j % NKK == 0 ? f32x16{} : sacc[j / NKK]);
+      } else {
+        constexpr int j = m - NQ - NS;
+        dpacc[j / NKK] = mfma_bf16(a, df[j % NKK], j % NKK == 0 ? f32x16{} : dpacc[j / NKK]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+  // Element phase of the tile at kv0 (register r of key block kb is key
+  // kv0 + 32 kb + 8 (r/4) + 4 g + r%4; a key is kept iff key <= min(kv_len - 1, qrow
+  // when causal)).
+  auto elements = [&](int kv0) __attribute__((always_inline)) {
+    if ((kv0 + BC > kv_len) || (p.causal && kv0 + BC - 1 > wrow0)) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const int lim = min(kv_len - 1, p.causal ? qrow : 0x3FFFFFFF) - kv0 - 32 * kb - 4 * g;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int off = 8 * (r >> 2) + (r & 3);
+          if (off > lim) sacc[kb][r] = kNegInf;
+        }
+      }
+    }
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float pr = fast_exp2(fmaf(sacc[kb][e], p.c, -lse2_q));
+        dpacc[kb][e] = pr * (dpacc[kb][e] - d_q);
+      }
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int h8 = 0; h8 < 2; ++h8) {
+        const f32x16& S = dpacc[kb];
+        const int o = 8 * h8;
+        dsb[2 * kb + h8] = pack_bf16x8(S[o], S[o + 1], S[o + 2], S[o + 3], S[o + 4], S[o + 5], S[o + 6], S[o + 7]);
+      }
+    // (keeps the phase's work inside it)
+#pragma unroll
+    for (int k = 0; k < 2 * NKB; ++k) asm volatile("" : "+v"(dsb[k]));
+  };
+
+  // Both groups run product phase t, barrier, element phase t, barrier; group 1 starts
+  // one barrier later, group 0 ends with one extra barrier.
+  if (nt > 0) {
+    if (gr == 0) wait_vmem();
+    __syncthreads();
+    if (gr == 1) __syncthreads();
+    auto tile = [&](int t, int jk, int jv, auto dq_flag) __attribute__((always_inline)) {
+      // K_t in buffer jk, V_t in jv; K_{t-1} in (jk + 2) % 3; tile t + 1 goes to
+      // K buffer (jk + 1) % 3 (it held K_{t-2}) and V buffer 1 - jv.
+      if (gr == 0) {
+        cp.issue(sT + kbuf((jk + 1) % 3) / 2, Kh, p.sn, kv0_of(t + 1), N);
+        cp.issue(sT + vbuf(1 - jv) / 2, Vh, p.sn, kv0_of(t + 1), N);
+      }
+      products(kbuf((jk + 2) % 3), kbuf(jk), vbuf(jv), dq_flag);
+      __syncthreads();
+      elements(kv0_of(t));
+      if (gr == 0) wait_vmem();
+      __syncthreads();
+    };
+    tile(0, 0, 0, Flag<false>{});
+    // Tiles 1.. (buffers K: t % 3, V: t % 2; six per trip so that every buffer offset is
+    // a constant).
+    for (int t = 1; t < nt; t += 6) {
+      tile(t, 1, 1, Flag<true>{});
+      if (t + 1 < nt) tile(t + 1, 2, 0, Flag<true>{});
+      if (t + 2 < nt) tile(t + 2, 0, 1, Flag<true>{});
+      if (t + 3 < nt) tile(t + 3, 1, 0, Flag<true>{});
+      if (t + 4 < nt) tile(t + 4, 2, 1, Flag<true>{});
+      if (t + 5 < nt) tile(t + 5, 0, 0, Flag<true>{});
+    }
+    // The last dQ products (tile nt - 1, its K in buffer (nt - 1) % 3).
+    {
+      const int kl = (nt - 1) % 3;
+      const int klast = kl == 0 ? kbuf(0) : (kl == 1 ? kbuf(1) : kbuf(2));
+      constexpr int AH = 2;
+      bf16x8 a0 = ta.read_tr(klast, 0, 0);
+      bf16x8 a1 = ta.read_tr(klast, 1 / NDB, 1 % NDB);
+#pragma unroll
+      for (int i = 0; i < NQM; ++i) {
+        const bf16x8 a = a0;
+        a0 = a1;
+        if (i + AH < NQM) a1 = ta.read_tr(klast, (i + AH) / NDB, (i + AH) % NDB);
+        lds_wait(2 * ((i + AH < NQM ? i + AH : NQM - 1) - i));
+        __builtin_amdgcn_sched_barrier(0);
+        dqacc[i % NDB] = mfma_bf16(a, dsb[i / NDB], dqacc[i % NDB]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    if (gr == 0) __syncthreads();
+  }
+
+  // dQ = scale dQ^T^T: lane = query, register r = dim 32 db + 8 (r/4) + 4 g + r%4.
+  if (qrow < N) {
+    bf16* dqrow = p.dq + base + (int64_t)qrow * p.sn;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        u32x2 w;
+        w[0] = pack_bf16x2(dqacc[db][4 * j] * p.scale, dqacc[db][4 * j + 1] * p.scale);
+        w[1] = pack_bf16x2(dqacc[db][4 * j + 2] * p.scale, dqacc[db][4 * j + 3] * p.scale);
+        *reinterpret_cast<u32x2*>(dqrow + db * 32 + 8 * j + 4 * g) = w;
+      }
+  }
+}
+
 // ------------------------------------------------------------------------------ launcher
 
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s) {
@@ -950,7 +1206,11 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s) {
     else if (drop) bwd_dq_kernel<128, FA_BWD_TILE_K_DROP_D128, false, false, true><<<grid, block, 0, s>>>(p);
     else if (sparse && smask) bwd_dq_kernel<128, TK128, true, true><<<grid, block, 0, s>>>(p);
     else if (sparse) bwd_dq_kernel<128, TK128, true><<<grid, block, 0, s>>>(p);
-    else bwd_dq_kernel<128, TK128, false><<<grid, block, 0, s>>>(p);
+    else if (FA_BWD_DQ_PINGPONG) {
+      BwdKParams pp = p;
+      pp.n_blocks = (a.N + kBwdRowsPP - 1) / kBwdRowsPP;
+      bwd_dq_pp_kernel<128, 64><<<dim3((unsigned)(a.B * a.H * pp.n_blocks)), dim3(512), 0, s>>>(pp);
+    } else bwd_dq_kernel<128, TK128, false><<<grid, block, 0, s>>>(p);
   } else {
     if (drop && sparse) bwd_dq_kernel<64, TK64, true, true, true><<<grid, block, 0, s>>>(p);
     else if (drop) bwd_dq_kernel<64, TK64, false, false, true><<<grid, block, 0, s>>>(p);

@@ -135,19 +135,20 @@ __device__ __forceinline__ float online_softmax_step(f32x16 (&s)[NKB], float c, 
 
 // ----------------------------------------------------------------------------------- bf16
 
-// acc + the sum of the 8 bf16 values of one packed operand (v_dot2 against ones).
-__device__ __forceinline__ float sum_bf16x8(bf16x8 v, float acc) {
+// Adds the 8 bf16 values of one packed operand to four partial sums (v_dot2 against
+// ones), one per 32-bit word (word i into acc[i]); the bf16 kernels combine them as
+// (acc0 + acc1) + (acc2 + acc3). (Through a scalar copy: this compiler's
+// __builtin_bit_cast of a vector element expression reads element 0 whatever the index.)
+__device__ __forceinline__ void sum_bf16x8_4(bf16x8 v, float (&acc)[4]) {
   const u32x4 u = __builtin_bit_cast(u32x4, v);
   const bf16x2 one = {(bf16)1.f, (bf16)1.f};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    // (Through a scalar copy: this compiler's __builtin_bit_cast of a vector
-    // element expression reads element 0 whatever the index.)
     const uint32_t w = u[i];
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), one, acc, false);
+    acc[i] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), one, acc[i], false);
   }
-  return acc;
 }
+__device__ __forceinline__ float sum4(const float (&acc)[4]) { return (acc[0] + acc[1]) + (acc[2] + acc[3]); }
 
 // The bf16 kernels' softmax step: as online_softmax_step, but the probabilities
 // are packed to bf16 (pb, the B operands of the P V product; k-step ks = 2 kb + s
@@ -171,7 +172,7 @@ __device__ __forceinline__ float softmax_tile_bf16(f32x16 (&s)[NKB], float c, fl
   const float m_use = (m_new == kNegInf) ? 0.f : m_new;
   const float alpha = fast_exp2(m_run - m_use);
   m_run = m_new;
-  float rs = 0.f, ru = 0.f;
+  float rs[4] = {0.f, 0.f, 0.f, 0.f}, ru[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -179,14 +180,14 @@ __device__ __forceinline__ float softmax_tile_bf16(f32x16 (&s)[NKB], float c, fl
 #pragma unroll
       for (int i = 8 * sh; i < 8 * sh + 8; ++i) {
         s[kb][i] = fast_exp2(fmaf(s[kb][i], c, -m_use));
-        ru += s[kb][i];
+        ru[i & 3] += s[kb][i];
       }
       pb[2 * kb + sh] = pack_bf16x8(s[kb][8 * sh + 0], s[kb][8 * sh + 1], s[kb][8 * sh + 2], s[kb][8 * sh + 3],
                                     s[kb][8 * sh + 4], s[kb][8 * sh + 5], s[kb][8 * sh + 6], s[kb][8 * sh + 7]);
-      rs = sum_bf16x8(pb[2 * kb + sh], rs);
+      sum_bf16x8_4(pb[2 * kb + sh], rs);
     }
-  l_run = l_run * alpha + rs;
-  lu_run = lu_run * alpha + ru;
+  l_run = l_run * alpha + sum4(rs);
+  lu_run = lu_run * alpha + sum4(ru);
   return alpha;
 }
 
@@ -370,7 +371,8 @@ void fwd_bf16_kernel(FwdKParams p) {
       const int voff = (int)(lds_address(vr) - lds_address(sT));
       bf16x8 a0 = ta.read_tr(voff, 0, 0);
       bf16x8 a1 = ta.read_tr(voff, 1 / NDB, 1 % NDB);
-      float mx0 = kNegInf, mx1 = kNegInf, m_new = 0.f, m_use = 0.f, alpha = 1.f, rs = 0.f, ru = 0.f;
+      float mx0 = kNegInf, mx1 = kNegInf, m_new = 0.f, m_use = 0.f, alpha = 1.f;
+      float rsp[4] = {0.f, 0.f, 0.f, 0.f}, rup[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int i = 0; i < NPV; ++i) {
         const bf16x8 a = a0;
@@ -396,13 +398,13 @@ void fwd_bf16_kernel(FwdKParams p) {
 #pragma unroll
           for (int e = s0; e < s1; ++e) {
             sacc[e / 16][e % 16] = fast_exp2(fmaf(sacc[e / 16][e % 16], p.c, -m_use));
-            ru += sacc[e / 16][e % 16];
+            rup[e & 3] += sacc[e / 16][e % 16];
             if ((e & 7) == 7) {  // a group of 8 probabilities is complete: pack and sum it
               const int kb = e / 16, s8 = (e % 16) / 8;
               pbn[2 * kb + s8] = pack_bf16x8(sacc[kb][8 * s8 + 0], sacc[kb][8 * s8 + 1], sacc[kb][8 * s8 + 2],
                                              sacc[kb][8 * s8 + 3], sacc[kb][8 * s8 + 4], sacc[kb][8 * s8 + 5],
                                              sacc[kb][8 * s8 + 6], sacc[kb][8 * s8 + 7]);
-              rs = sum_bf16x8(pbn[2 * kb + s8], rs);
+              sum_bf16x8_4(pbn[2 * kb + s8], rsp);
             }
           }
         }
@@ -412,6 +414,7 @@ void fwd_bf16_kernel(FwdKParams p) {
       // rescale branch, out of the slices they were placed in.
 #pragma unroll
       for (int i = 0; i < 2 * NKB; ++i) asm volatile("" : "+v"(pbn[i]));
+      float rs = sum4(rsp), ru = sum4(rup);
       asm volatile("" : "+v"(rs), "+v"(ru), "+v"(alpha), "+v"(m_new));
       if (DROP) drop_tile(pbn, kv0);
       const float m_prev = m_run;
@@ -442,6 +445,256 @@ void fwd_bf16_kernel(FwdKParams p) {
   const float l_tot = pair_sum(l_run);
   const float lu_tot = pair_sum(lu_run);
   const float inv = l_tot > 0.f ? (DROP ? p.drop.scale : 1.f) / l_tot : 0.f;
+  if (qrow < N) {
+    bf16* Orow = static_cast<bf16*>(p.o) + base + (int64_t)qrow * p.sn;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        u32x2 w;
+        w[0] = pack_bf16x2(oacc[db][4 * j + 0] * inv, oacc[db][4 * j + 1] * inv);
+        w[1] = pack_bf16x2(oacc[db][4 * j + 2] * inv, oacc[db][4 * j + 3] * inv);
+        *reinterpret_cast<u32x2*>(Orow + db * 32 + 8 * j + 4 * g) = w;
+      }
+    if (g == 0)
+      p.lse[(int64_t)inst * N + qrow] = lu_tot > 0.f ? (m_run + fast_log2(lu_tot)) * kLn2 : kNegInf;
+  }
+}
+
+// -------------------------------------------------------------------- bf16, two wave groups
+
+// The forward with the products and the softmax in different waves at any one time.
+// A workgroup of 8 waves owns 256 query rows: waves w and w + 4 share a SIMD and form
+// two groups (w < 4 and w >= 4) that run half a key tile apart. In one phase group 0
+// issues the products of tile t (S(t) = K_t Q^T, then the P V of tile t - 1) while
+// group 1 runs the softmax of tile t - 1; in the next phase the roles swap (workgroup
+// barriers separate the phases). A wave that only issues products (and their operand
+// reads) keeps the matrix core busy while the wave beside it on the SIMD issues its
+// VALU work, so each SIMD overlaps the two kinds of work instead of interleaving them
+// inside one instruction stream. The arithmetic is that of fwd_bf16_kernel in the same
+// order (same products per accumulator, same row-sum chains), so the two kernels give
+// the same bits.
+// Wave (group gr, index wg) owns the 32 rows q0 + 64 wg + 32 gr ..: the two waves of a
+// SIMD see the same key tiles, and both groups visit the same tiles of the diagonal.
+// K/V tiles are double-buffered and copied by group 0 at the start of its product
+// phases: phase t issues tile t + 1's K and tile t's V, waited for at the end of
+// group 0's softmax phase t.
+constexpr int kFwdRowsPP = 256;
+#ifndef FA_FWD_PP_AHEAD
+#define FA_FWD_PP_AHEAD 4
+#endif
+
+template <int D, int BC>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
+void fwd_pp_kernel(FwdKParams p) {
+  constexpr int NKB = BC / 32;
+  constexpr int NDB = D / 32;
+  constexpr int NKK = D / 16;
+  constexpr int TILE = BC * D;
+  constexpr int NS = NKK * NKB;          // S products per tile
+  constexpr int NPV = NDB * (BC / 16);   // P V products per tile
+  constexpr int NE = NKB * 16;           // scores per lane and tile
+  __shared__ __attribute__((aligned(16))) bf16 sT[4 * TILE];  // [K0 | K1 | V0 | V1]
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = uniform_wave_id();
+  const int gr = wave >> 2, wg = wave & 3;
+  const int l32 = lane & 31, g = lane >> 5;
+  const int N = p.N;
+  int inst, rank;
+  schedule_tile(blockIdx.x, p.B * p.H, p.n_qblocks, inst, rank);
+  const int qb = p.causal ? (p.n_qblocks - 1 - rank) : rank;
+  const int b = inst / p.H, h = inst - b * p.H;
+  const int64_t base = (int64_t)b * p.sb + (int64_t)h * p.sh;
+  const bf16* Qh = static_cast<const bf16*>(p.q) + base;
+  const bf16* Kh = static_cast<const bf16*>(p.k) + base;
+  const bf16* Vh = static_cast<const bf16*>(p.v) + base;
+  const int q0 = qb * kFwdRowsPP;
+  const int wrow0 = q0 + 64 * wg + 32 * gr;  // this wave's first row
+  const int qrow = wrow0 + l32;
+  int kv_len = N;
+  if (p.key_len) kv_len = min(max(p.key_len[b], 0), N);
+  int kv_end = kv_len;
+  if (p.causal) kv_end = min(kv_end, q0 + kFwdRowsPP);
+  const int nt = kv_end > 0 ? (kv_end + BC - 1) / BC : 0;
+
+  // This lane's query (B operand of S^T = K Q^T; slot group g of k-step kk holds
+  // dims [16 kk + 8 g, +8)); rows past N are clamped and never stored.
+  bf16x8 qf[NKK];
+  const int64_t qoff = (int64_t)min(qrow, N - 1) * p.sn;
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(Qh + qoff + 16 * kk + 8 * g);
+
+  f32x16 oacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+  float m_run = kNegInf, l_run = 0.f, lu_run = 0.f;
+  f32x16 sacc[NKB];
+  bf16x8 pb[2 * NKB];
+
+  TileCopy<BC, D, 4> cp;
+  cp.init(wg, lane, p.sn);
+  TileAddr<D> ta;
+  {
+    TileOffsets<D> to;
+    to.init(lane);
+    ta.init(to, lds_address(sT));
+  }
+  auto kv0_of = [&](int t) { return min(t, nt - 1) * BC; };
+  constexpr int KB0 = 0, KB1 = 2 * TILE, VB0 = 4 * TILE, VB1 = 6 * TILE;  // byte offsets in sT
+
+  // Product phase: S(t) from the K buffer at byte offset kb, then (PV) the P V product
+  // of the previous tile from the V buffer at vb. Every LDS operand is an inline-assembly
+  // read issued AH products ahead and waited for exactly (reads return in order).
+  auto products = [&](int kb, int vb, auto pv_flag) __attribute__((always_inline)) {
+    constexpr bool PV = decltype(pv_flag)::value;
+    constexpr int NM = NS + (PV ? NPV : 0), AH = FA_FWD_PP_AHEAD;
+    bf16x8 ra[AH + 1];
+    int ia[AH + 1];
+    int nrd = 0;
+    auto fetch = [&](int m) __attribute__((always_inline)) {
+      const int sl = m % (AH + 1);
+      if (m < NS) {
+        ra[sl] = ta.read_row(kb, m % NKB, m / NKB);
+        nrd += 1;
+      } else {
+        const int i = m - NS;
+        ra[sl] = ta.read_tr(vb, i / NDB, i % NDB);
+        nrd += 2;
+      }
+      ia[sl] = nrd - 1;
+    };
+#pragma unroll
+    for (int m = 0; m < AH && m < NM; ++m) fetch(m);
+    static_for<NM>([&](auto mc) __attribute__((always_inline)) {
+      constexpr int m = decltype(mc)::value;
+      if (m + AH < NM) fetch(m + AH);
+      lds_wait(nrd - 1 - ia[m % (AH + 1)]);
+      __builtin_amdgcn_sched_barrier(0);
+      const bf16x8 a = ra[m % (AH + 1)];
+      if constexpr (m < NS) {
+        sacc[m % NKB] = mfma_bf16(a, qf[m / NKB], m < NKB ? f32x16{} : sacc[m % NKB]);
+      } else {
+        constexpr int i = m - NS;
+        oacc[i % NDB] = mfma_bf16(a, pb[i / NDB], oacc[i % NDB]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+
+  // Softmax phase of the tile at kv0: mask (only where the tile needs it), row max,
+  // reference point, exponentials, both row sums (four partial sums each, combined as in
+// fwd_bf16_kernel), bf16
+  // packing into pb, and the rescale of O when a row's reference point moved.
+  auto softmax = [&](int kv0) __attribute__((always_inline)) {
+    if ((kv0 + BC > kv_len) || (p.causal && kv0 + BC - 1 > wrow0)) mask_tile<NKB>(sacc, kv0, kv_len, p.causal, qrow, g);
+    float t8[NE / 4];
+#pragma unroll
+    for (int i = 0; i < NE / 4; ++i) {
+      const int e = 4 * i;
+      t8[i] = fmaxf(fmaxf(sacc[e / 16][e % 16], sacc[e / 16][e % 16 + 1]),
+                    fmaxf(sacc[e / 16][e % 16 + 2], sacc[e / 16][e % 16 + 3]));
+    }
+#pragma unroll
+    for (int w = NE / 8; w >= 1; w /= 2)
+#pragma unroll
+      for (int i = 0; i < w; ++i) t8[i] = fmaxf(t8[i], t8[i + w]);
+    const float mx = pair_max(t8[0]);
+    const float mxs = (mx == kNegInf) ? kNegInf : mx * p.c;
+    const float m_new = (mxs > m_run + kRescaleSlack) ? mxs : m_run;
+    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - m_use);
+    float rs[4] = {0.f, 0.f, 0.f, 0.f}, ru[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+      sacc[e / 16][e % 16] = fast_exp2(fmaf(sacc[e / 16][e % 16], p.c, -m_use));
+      ru[e & 3] += sacc[e / 16][e % 16];
+    }
+#pragma unroll
+    for (int k = 0; k < 2 * NKB; ++k) {
+      const int kb = k / 2, s8 = 8 * (k % 2);
+      pb[k] = pack_bf16x8(sacc[kb][s8 + 0], sacc[kb][s8 + 1], sacc[kb][s8 + 2], sacc[kb][s8 + 3], sacc[kb][s8 + 4],
+                          sacc[kb][s8 + 5], sacc[kb][s8 + 6], sacc[kb][s8 + 7]);
+      sum_bf16x8_4(pb[k], rs);
+    }
+    const float m_prev = m_run;
+    m_run = m_new;
+    l_run = l_run * alpha + sum4(rs);
+    lu_run = lu_run * alpha + sum4(ru);
+    if (__builtin_amdgcn_ballot_w64(m_run != m_prev)) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+    }
+    // (keeps the phase's work inside it: nothing may sink past the barrier's wait)
+#pragma unroll
+    for (int k = 0; k < 2 * NKB; ++k) asm volatile("" : "+v"(pb[k]));
+    asm volatile("" : "+v"(l_run), "+v"(lu_run));
+  };
+
+  // Both groups run the same sequence (product phase t, barrier, softmax phase t,
+  // barrier); group 1 starts one barrier later, which puts each group's products beside
+  // the other group's softmax. Group 0 ends with one extra barrier so that both groups
+  // meet the same number.
+  if (nt > 0) {
+    if (gr == 0) {
+      cp.issue(sT + KB0 / 2, Kh, p.sn, kv0_of(0), N);
+      wait_vmem();
+    }
+    __syncthreads();
+    if (gr == 1) __syncthreads();
+    // Tile 0 (no P V yet).
+    if (gr == 0) {
+      cp.issue(sT + KB1 / 2, Kh, p.sn, kv0_of(1), N);
+      cp.issue(sT + VB0 / 2, Vh, p.sn, kv0_of(0), N);
+    }
+    products(KB0, VB1, Flag<false>{});
+    __syncthreads();
+    softmax(kv0_of(0));
+    if (gr == 0) wait_vmem();
+    __syncthreads();
+    // Tile t >= 1: K_t in kb, V_{t-1} in vbp; group 0 copies K_{t+1} into kbn and V_t
+    // into vb (two per trip so that every buffer offset is a constant).
+    auto tile = [&](int t, int kb, int kbn, int vb, int vbp) __attribute__((always_inline)) {
+      if (gr == 0) {
+        cp.issue(sT + kbn / 2, Kh, p.sn, kv0_of(t + 1), N);
+        cp.issue(sT + vb / 2, Vh, p.sn, kv0_of(t), N);
+      }
+      products(kb, vbp, Flag<true>{});
+      __syncthreads();
+      softmax(kv0_of(t));
+      if (gr == 0) wait_vmem();
+      __syncthreads();
+    };
+    for (int t = 1; t < nt; t += 2) {
+      tile(t, KB1, KB0, VB1, VB0);
+      if (t + 1 < nt) tile(t + 1, KB0, KB1, VB0, VB1);
+    }
+    // The last P V (tile nt - 1, its V in buffer (nt - 1) % 2).
+    const int vlast = ((nt - 1) & 1) ? VB1 : VB0;
+    {
+      constexpr int AH = 2;
+      bf16x8 a0 = ta.read_tr(vlast, 0, 0);
+      bf16x8 a1 = ta.read_tr(vlast, 1 / NDB, 1 % NDB);
+#pragma unroll
+      for (int i = 0; i < NPV; ++i) {
+        const bf16x8 a = a0;
+        a0 = a1;
+        if (i + AH < NPV) a1 = ta.read_tr(vlast, (i + AH) / NDB, (i + AH) % NDB);
+        lds_wait(2 * ((i + AH < NPV ? i + AH : NPV - 1) - i));
+        __builtin_amdgcn_sched_barrier(0);
+        oacc[i % NDB] = mfma_bf16(a, pb[i / NDB], oacc[i % NDB]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    if (gr == 0) __syncthreads();
+  }
+
+  // Epilogue: O = O_acc / l (the rounded weights' sum), LSE = (m + log2 lu) ln 2.
+  const float l_tot = pair_sum(l_run);
+  const float lu_tot = pair_sum(lu_run);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (qrow < N) {
     bf16* Orow = static_cast<bf16*>(p.o) + base + (int64_t)qrow * p.sn;
 #pragma unroll
@@ -612,6 +865,16 @@ static FwdKParams make_params(const FwdArgs& a) {
 #ifndef FA_FWD_BC_D64
 #define FA_FWD_BC_D64 64
 #endif
+// Dense d = 128 (no dropout): the two-group kernel and its key tile.
+#ifndef FA_FWD_PINGPONG
+#define FA_FWD_PINGPONG 1
+#endif
+#ifndef FA_FWD_PP_BC
+#define FA_FWD_PP_BC 64
+#endif
+#ifndef FA_FWD_PP_AHEAD
+#define FA_FWD_PP_AHEAD 4
+#endif
 // Block-sparse d = 64: one 128-key tile per 128-key block (no masked tiles there).
 #ifndef FA_FWD_BC_SPARSE_D64
 #define FA_FWD_BC_SPARSE_D64 128
@@ -634,7 +897,11 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s) {
   } else if (a.d == 128) {
     if (sparse && smask) fwd_bf16_kernel<128, BC128, true, true><<<grid, block, 0, s>>>(p);
     else if (sparse) fwd_bf16_kernel<128, BC128, true><<<grid, block, 0, s>>>(p);
-    else fwd_bf16_kernel<128, BC128, false><<<grid, block, 0, s>>>(p);
+    else if (FA_FWD_PINGPONG) {
+      FwdKParams pp = p;
+      pp.n_qblocks = (a.N + kFwdRowsPP - 1) / kFwdRowsPP;
+      fwd_pp_kernel<128, FA_FWD_PP_BC><<<dim3((unsigned)(a.B * a.H * pp.n_qblocks)), dim3(512), 0, s>>>(pp);
+    } else fwd_bf16_kernel<128, BC128, false><<<grid, block, 0, s>>>(p);
   } else {
     if (sparse && smask) fwd_bf16_kernel<64, BCS64, true, true><<<grid, block, 0, s>>>(p);
     else if (sparse) fwd_bf16_kernel<64, BCS64, true><<<grid, block, 0, s>>>(p);
