@@ -559,6 +559,10 @@ void bwd_dkdv_kernel(BwdKParams p) {
 #ifndef FA_BWD_TILE_K_D64
 #define FA_BWD_TILE_K_D64 64
 #endif
+// Dense d = 128 without dropout: the dK/dV pass as two wave groups (bwd_dkdv_pp_kernel).
+#ifndef FA_BWD_DKDV_PINGPONG
+#define FA_BWD_DKDV_PINGPONG 1
+#endif
 // Dense d = 128 without dropout: the dQ pass as two wave groups (bwd_dq_pp_kernel).
 #ifndef FA_BWD_DQ_PINGPONG
 #define FA_BWD_DQ_PINGPONG 1
@@ -905,6 +909,260 @@ void bwd_dq_kernel(BwdKParams p) {
   }
 }
 
+// ------------------------------------------------------------ dK, dV, two wave groups
+
+// The dK/dV pass with the products and the element work in different waves at any one
+// time (the scheme of the two-group forward): 8 waves own 256 keys, waves w and w + 4
+// share a SIMD and form two groups that run half a query tile apart, separated by
+// workgroup barriers. Wave (group gr, index wg) owns the 32 keys k0 + 64 wg + 32 gr ..
+//   product phase t:  dV^T += dO_{t-1}^T P(t - 1), dK^T += Q_{t-1}^T dS(t - 1),
+//                     S(t) = Q_t K^T, dP(t) = dO_t V^T;
+//   element phase t:  mask, P = 2^(c S - lse2), dS = P (dP - D), bf16 packing.
+// The products and the element work per tile are those of bwd_dkdv_kernel, in the same
+// order per accumulator, so the two kernels give the same bits. The key block's V
+// (256 rows) stays in LDS; Q/dO tiles and their row statistics are triple-buffered
+// (tile t - 1's are read by the products of phase t) and copied by group 0 during its
+// product phase t (tile t + 1), waited for at the end of its element phase t.
+constexpr int kBwdKeysPP = 256;
+#ifndef FA_BWD_DKDV_PP_AHEAD
+#define FA_BWD_DKDV_PP_AHEAD 2
+#endif
+
+template <int D, int BRQ>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
+void bwd_dkdv_pp_kernel(BwdKParams p) {
+  constexpr int NDB = D / 32;
+  constexpr int NKK = D / 16;
+  constexpr int TILE = BRQ * D;
+  static_assert(BRQ == 32, "one 32-query block per tile");
+  constexpr int NSM = NKK;       // S products (as many dP products)
+  constexpr int NVM = 2 * NDB;   // dV products (as many dK products)
+  // [Q0 | dO0 | Q1 | dO1 | Q2 | dO2], then the key block's V.
+  __shared__ __attribute__((aligned(16))) bf16 sT[6 * TILE];
+  __shared__ __attribute__((aligned(16))) bf16 sV[kBwdKeysPP * D];
+  __shared__ __attribute__((aligned(16))) float sL[3][64];
+  __shared__ __attribute__((aligned(16))) float sDl[3][64];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = uniform_wave_id();
+  const int gr = wave >> 2, wg = wave & 3;
+  const int l32 = lane & 31, g = lane >> 5;
+  const int N = p.N;
+  int inst, rank;
+  schedule_tile(blockIdx.x, p.B * p.H, p.n_blocks, inst, rank);
+  const int b = inst / p.H, h = inst - b * p.H;
+  const int64_t base = (int64_t)b * p.sb + (int64_t)h * p.sh;
+  const bf16* Qh = p.q + base;
+  const bf16* Kh = p.k + base;
+  const bf16* Vh = p.v + base;
+  const bf16* dOh = p.dout + base;
+  const int k0 = rank * kBwdKeysPP;  // causal: the lowest key blocks see the most queries; they go first
+  const int kw0 = k0 + 64 * wg + 32 * gr;  // this wave's 32 keys
+  const int mykey = kw0 + l32;
+  const int64_t rowbase = (int64_t)inst * N;
+  int kv_len = N;
+  if (p.key_len) kv_len = min(max(p.key_len[b], 0), N);
+  const int qt_begin = p.causal ? k0 / BRQ : 0;
+  const int n_qt = k0 >= kv_len ? 0 : (N + BRQ - 1) / BRQ - qt_begin;
+  auto tile_q0 = [&](int t) { return (qt_begin + min(t, n_qt - 1)) * BRQ; };
+
+  f32x16 dkacc[NDB], dvacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      dkacc[db][r] = 0.f;
+      dvacc[db][r] = 0.f;
+    }
+
+  if (n_qt > 0) {
+    // This wave's K as the B operand of S = Q K^T (lane column = mykey; slot group g of
+    // k-step kk holds dims [16 kk + 8 g, +8)); its V rows are read from LDS.
+    bf16x8 kf[NKK];
+    const int64_t koff = (int64_t)min(mykey, N - 1) * p.sn + 8 * g;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) kf[kk] = *reinterpret_cast<const bf16x8*>(Kh + koff + 16 * kk);
+    {
+      TileCopy<kBwdKeysPP, D, 8> cpv;  // keys past the end are clamped (their P is 0)
+      cpv.init(wave, lane, p.sn);
+      cpv.issue(sV, Vh, p.sn, k0, N);
+    }
+    TileCopy<BRQ, D, 4> cp;
+    cp.init(wg, lane, p.sn);
+    TileAddr<D> ta;
+    {
+      TileOffsets<D> to;
+      to.init(lane);
+      ta.init(to, lds_address(sT));
+    }
+    auto qbuf = [](int j) { return 4 * TILE * j; };            // byte offsets in sT
+    auto dobuf = [](int j) { return 4 * TILE * j + 2 * TILE; };
+    // (opaque, so that the V row addresses are not hoisted into registers per k-step)
+    uint32_t vdelta = lds_address(sV) - lds_address(sT) + (uint32_t)(2 * wg + gr) * (64 * D);
+    asm volatile("" : "+s"(vdelta));
+    auto issue_tile = [&](int t, int j) __attribute__((always_inline)) {
+      const int q0 = tile_q0(t);
+      cp.issue(sT + qbuf(j) / 2, Qh, p.sn, q0, N);
+      cp.issue(sT + dobuf(j) / 2, dOh, p.sn, q0, N);
+      if (wg == 0) vec_dma64(sL[j], p.lse2 + rowbase, q0, N, lane);
+      if (wg == 1) vec_dma64(sDl[j], p.delta + rowbase, q0, N, lane);
+    };
+
+    f32x16 sacc, dpacc;
+    bf16x8 pb[2], dsb[2];
+    // Product phase: (DKV) dV, dK of the previous tile from buffer jp, then S, dP of this
+    // tile from buffer j. Every LDS operand is an inline-assembly read issued AH products
+    // ahead and waited for exactly.
+    auto products = [&](int j, int jp, auto dkv_flag) __attribute__((always_inline)) {
+      constexpr bool DKV = decltype(dkv_flag)::value;
+      constexpr int NP = DKV ? 2 * NVM : 0;
+      constexpr int NM = NP + 2 * NSM, AH = FA_BWD_DKDV_PP_AHEAD;
+      const int qo = qbuf(j), doo = dobuf(j), qop = qbuf(jp), doop = dobuf(jp);
+      bf16x8 ra[AH + 1], rb[AH + 1];
+      int ia[AH + 1];
+      int nrd = 0;
+      auto fetch = [&](int m) __attribute__((always_inline)) {
+        const int sl = m % (AH + 1);
+        if (m < NP) {
+          const int i = m % NVM;
+          ra[sl] = ta.read_tr(m < NVM ? doop : qop, i / NDB, i % NDB);
+          nrd += 2;
+        } else if (m < NP + NSM) {
+          const int jj = m - NP;
+          ra[sl] = ta.read_row(qo, 0, jj);
+          nrd += 1;
+        } else {
+          const int jj = m - NP - NSM;
+          ra[sl] = ta.read_row(doo, 0, jj);
+          rb[sl] = lds_read_b128_asm(ta.row[jj] + vdelta, 0);
+          nrd += 2;
+        }
+        ia[sl] = nrd - 1;
+      };
+#pragma unroll
+      for (int m = 0; m < AH; ++m) fetch(m);
+      static_for<NM>([&](auto mc) __attribute__((always_inline)) {
+        constexpr int m = decltype(mc)::value;
+        if (m + AH < NM) fetch(m + AH);
+        lds_wait(nrd - 1 - ia[m % (AH + 1)]);
+        __builtin_amdgcn_sched_barrier(0);
+        const bf16x8 a = ra[m % (AH + 1)];
+        if constexpr (DKV && m < NVM) {
+          dvacc[m % NDB] = mfma_bf16(a, pb[m / NDB], dvacc[m % NDB]);
+        } else if constexpr (m < NP) {
+          constexpr int i = m - NVM;
+          dkacc[i % NDB] = mfma_bf16(a, dsb[i / NDB], dkacc[i % NDB]);
+        } else if constexpr (m < NP + NSM) {
+          constexpr int jj = m - NP;
+          sacc = mfma_bf16(a, kf[jj], jj == 0 ? f32x16{} : sacc);
+        } else {
+          constexpr int jj = m - NP - NSM;
+          dpacc = mfma_bf16(a, rb[m % (AH + 1)], jj == 0 ? f32x16{} : dpacc);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    };
+    // Element phase of tile t (register r is query q0 + 8 (r/4) + 4 g + r%4; kept iff
+    // lo <= its offset <= hi, as in bwd_dkdv_kernel), stats from buffer j.
+    auto elements = [&](int t, int j) __attribute__((always_inline)) {
+      const int q0 = tile_q0(t);
+      if ((p.causal && q0 < kw0 + 31) || (kw0 + 32 > kv_len) || (q0 + BRQ > N)) {
+        const int lo = mykey < kv_len ? (p.causal ? mykey : 0) - q0 - 4 * g : 0x3FFFFFFF;
+        const int hi = N - 1 - q0 - 4 * g;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int off = 8 * (r >> 2) + (r & 3);
+          if (off < lo || off > hi) sacc[r] = kNegInf;
+        }
+      }
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const f32x4 lv = *reinterpret_cast<const f32x4*>(&sL[j][8 * jj + 4 * g]);
+        const f32x4 dv = *reinterpret_cast<const f32x4*>(&sDl[j][8 * jj + 4 * g]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 4 * jj + i;
+          sacc[r] = fast_exp2(fmaf(sacc[r], p.c, -lv[i]));
+          dpacc[r] = sacc[r] * (dpacc[r] - dv[i]);
+        }
+      }
+#pragma unroll
+      for (int h8 = 0; h8 < 2; ++h8) {
+        const int o = 8 * h8;
+        pb[h8] = pack_bf16x8(sacc[o], sacc[o + 1], sacc[o + 2], sacc[o + 3], sacc[o + 4], sacc[o + 5], sacc[o + 6],
+                             sacc[o + 7]);
+        dsb[h8] = pack_bf16x8(dpacc[o], dpacc[o + 1], dpacc[o + 2], dpacc[o + 3], dpacc[o + 4], dpacc[o + 5],
+                              dpacc[o + 6], dpacc[o + 7]);
+      }
+      // (keeps the phase's work inside it)
+      asm volatile("" : "+v"(pb[0]), "+v"(pb[1]), "+v"(dsb[0]), "+v"(dsb[1]));
+    };
+
+    // Both groups run product phase t, barrier, element phase t, barrier; group 1 starts
+    // one barrier later, group 0 ends with one extra barrier.
+    if (gr == 0) issue_tile(0, 0);
+    wait_vmem();  // (V, and tile 0 for group 0)
+    __syncthreads();
+    if (gr == 1) __syncthreads();
+    auto tile = [&](int t, int j, auto dkv_flag) __attribute__((always_inline)) {
+      // tile t in buffer j, tile t - 1 in (j + 2) % 3; tile t + 1 goes to (j + 1) % 3
+      if (gr == 0) issue_tile(t + 1, (j + 1) % 3);
+      products(j, (j + 2) % 3, dkv_flag);
+      __syncthreads();
+      elements(t, j);
+      if (gr == 0) wait_vmem();
+      __syncthreads();
+    };
+    tile(0, 0, Flag<false>{});
+    for (int t = 1; t < n_qt; t += 3) {
+      tile(t, 1, Flag<true>{});
+      if (t + 1 < n_qt) tile(t + 1, 2, Flag<true>{});
+      if (t + 2 < n_qt) tile(t + 2, 0, Flag<true>{});
+    }
+    // The last dV, dK products (tile n_qt - 1, in buffer (n_qt - 1) % 3).
+    {
+      const int jl = (n_qt - 1) % 3;
+      const int qol = jl == 0 ? qbuf(0) : (jl == 1 ? qbuf(1) : qbuf(2));
+      const int dol = jl == 0 ? dobuf(0) : (jl == 1 ? dobuf(1) : dobuf(2));
+#pragma unroll
+      for (int i = 0; i < NVM; ++i) {
+        const bf16x8 a = ta.read_tr(dol, i / NDB, i % NDB);
+        lds_wait(0);
+        __builtin_amdgcn_sched_barrier(0);
+        dvacc[i % NDB] = mfma_bf16(a, pb[i / NDB], dvacc[i % NDB]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int i = 0; i < NVM; ++i) {
+        const bf16x8 a = ta.read_tr(qol, i / NDB, i % NDB);
+        lds_wait(0);
+        __builtin_amdgcn_sched_barrier(0);
+        dkacc[i % NDB] = mfma_bf16(a, dsb[i / NDB], dkacc[i % NDB]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    if (gr == 0) __syncthreads();
+  }
+
+  // dK = scale (dK^T)^T, dV: lane column = mykey, register r = dim 32 db + 8 (r/4) + 4 g + r%4.
+  if (mykey < N) {
+    bf16* dkrow = p.dk + base + (int64_t)mykey * p.sn;
+    bf16* dvrow = p.dv + base + (int64_t)mykey * p.sn;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        u32x2 wk, wv;
+        wk[0] = pack_bf16x2(dkacc[db][4 * j] * p.scale, dkacc[db][4 * j + 1] * p.scale);
+        wk[1] = pack_bf16x2(dkacc[db][4 * j + 2] * p.scale, dkacc[db][4 * j + 3] * p.scale);
+        wv[0] = pack_bf16x2(dvacc[db][4 * j], dvacc[db][4 * j + 1]);
+        wv[1] = pack_bf16x2(dvacc[db][4 * j + 2], dvacc[db][4 * j + 3]);
+        *reinterpret_cast<u32x2*>(dkrow + db * 32 + 8 * j + 4 * g) = wk;
+        *reinterpret_cast<u32x2*>(dvrow + db * 32 + 8 * j + 4 * g) = wv;
+      }
+  }
+}
+
 // --------------------------------------------------------------- dQ, two wave groups
 
 // The dQ pass with the products and the element work in different waves at any one
@@ -1228,7 +1486,11 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s) {
     else if (drop) bwd_dkdv_kernel<128, TQ128, false, true, false, true><<<grid, block, 0, s>>>(p);
     else if (sparse && smask) bwd_dkdv_kernel<128, TQ128, true, true, true><<<grid, block, 0, s>>>(p);
     else if (sparse) bwd_dkdv_kernel<128, TQ128, true, true><<<grid, block, 0, s>>>(p);
-    else bwd_dkdv_kernel<128, TQ128, false, true><<<grid, block, 0, s>>>(p);
+    else if (FA_BWD_DKDV_PINGPONG && TQ128 == 32) {
+      BwdKParams pp = p;
+      pp.n_blocks = (a.N + kBwdKeysPP - 1) / kBwdKeysPP;
+      bwd_dkdv_pp_kernel<128, 32><<<dim3((unsigned)(a.B * a.H * pp.n_blocks)), dim3(512), 0, s>>>(pp);
+    } else bwd_dkdv_kernel<128, TQ128, false, true><<<grid, block, 0, s>>>(p);
   } else {
     if (drop && sparse) bwd_dkdv_kernel<64, TQ64, true, false, true, true><<<grid, block, 0, s>>>(p);
     else if (drop) bwd_dkdv_kernel<64, TQ64, false, false, false, true><<<grid, block, 0, s>>>(p);
