@@ -178,8 +178,9 @@ def step_traffic_for(workload: str):
 
 
 # Library timer names of the kernels, by a fragment of their symbol.
-KERNEL_NAMES = {"fwd_bf16_kernel": "fa_fwd_bf16", "fwd_f32_kernel": "fa_fwd_f32",
-                "bwd_dkdv_kernel": "fa_bwd_dkdv", "bwd_dq_kernel": "fa_bwd_dq"}
+KERNEL_NAMES = {"fwd_bf16_kernel": "fa_fwd_bf16", "fwd_pp_kernel": "fa_fwd_bf16", "fwd_f32_kernel": "fa_fwd_f32",
+                "bwd_dkdv_kernel": "fa_bwd_dkdv", "bwd_dkdv_pp_kernel": "fa_bwd_dkdv",
+                "bwd_dq_kernel": "fa_bwd_dq", "bwd_dq_pp_kernel": "fa_bwd_dq"}
 
 
 def calibrate_copy(nbytes: int = 1 << 30, launches: int = 3):
