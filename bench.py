@@ -133,7 +133,7 @@ def sq_digest(p1: str, p2: str, workload: str):
     import csv
     import glob
     import re
-    vals = {}
+    vals, clocks = {}, {}
     for d in (p1, p2):
         for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
             with open(f) as fh:
@@ -141,6 +141,10 @@ def sq_digest(p1: str, p2: str, workload: str):
                     k = re.sub(r"^void fa::", "", row["Kernel_Name"])
                     k = k.replace("(fa::FwdKParams)", "").replace("(fa::BwdKParams)", "")
                     vals.setdefault(k, {}).setdefault(row["Counter_Name"], []).append(float(row["Counter_Value"]))
+                    dur = int(row.get("End_Timestamp") or 0) - int(row.get("Start_Timestamp") or 0)
+                    if row["Counter_Name"] == "GRBM_GUI_ACTIVE" and dur > 0:
+                        # engine cycles per XCD over the dispatch's nanoseconds: the clock it ran at
+                        clocks.setdefault(k, []).append(float(row["Counter_Value"]) / 8 / dur * 1e3)
     out = {"workload": workload, "sources_hash": sources_hash(), "kernels": {}}
     lines = []
     for k, cs in vals.items():
@@ -154,12 +158,17 @@ def sq_digest(p1: str, p2: str, workload: str):
                "waiting": round(m["SQ_WAIT_ANY"] / w, 3), "issue_stalled": round(m["SQ_WAIT_INST_ANY"] / w, 3),
                "valu_per_mfma": round((m["SQ_INSTS_VALU"] - mf) / mf, 2), "lds_per_mfma": round(m["SQ_INSTS_LDS"] / mf, 2),
                "salu_per_mfma": round(m["SQ_INSTS_SALU"] / mf, 2), "lds_bank_conflicts": m["SQ_LDS_BANK_CONFLICT"]}
+        if clocks.get(k):
+            ck = sorted(clocks[k])
+            rec["engine_clock_mhz"] = round(ck[len(ck) // 2])
         out["kernels"][name] = rec
         lines += [k, "  " + "  ".join(f"{c}={m[c]:.4g}" for c in sorted(m)),
                   f"  mfma_busy {busy:.3f}; wave time: issuing {rec['issuing']:.2f}, waiting {rec['waiting']:.2f}, "
                   f"issue-stalled {rec['issue_stalled']:.2f}; per MFMA: {rec['valu_per_mfma']:.2f} other VALU, "
                   f"{rec['lds_per_mfma']:.2f} LDS, {rec['salu_per_mfma']:.2f} SALU; LDS bank conflicts "
-                  f"{m['SQ_LDS_BANK_CONFLICT']:.0f}", ""]
+                  f"{m['SQ_LDS_BANK_CONFLICT']:.0f}"
+                  + (f"; engine clock {rec['engine_clock_mhz']} MHz (median over dispatches of GRBM_GUI_ACTIVE / 8 "
+                     f"over the dispatch's duration)" if "engine_clock_mhz" in rec else ""), ""]
     return out, "\n".join(lines)
 
 
@@ -730,6 +739,20 @@ def main():
                                            "GRBM_GUI_ACTIVE / 8") if live_sq is not None
                                else counter_source("sq_counters", args.workload, sq))
 
+    # The engine clock each kernel ran at (the published peak assumes 2.4 GHz; under this load the
+    # chip runs slower), and the MFMA peak at that clock.
+    engine_clock = None
+    if sq is not None and any("engine_clock_mhz" in v for v in sq["kernels"].values()):
+        engine_clock = {k: v["engine_clock_mhz"] for k, v in sq["kernels"].items() if "engine_clock_mhz" in v}
+        rk = roofline.get("kernel")
+        if rk in engine_clock:
+            at_clock = PEAK_BF16_TFLOPS * engine_clock[rk] / 2400.0
+            engine_clock["roofline_kernel_peak_at_clock"] = round(at_clock, 1)
+            engine_clock["roofline_kernel_frac_at_clock"] = round(roofline["achieved"] / at_clock, 4)
+        engine_clock["unit"] = "MHz"
+        engine_clock["source"] = mfma_busy["source"].replace(
+            "SQ_VALU_MFMA_BUSY_CYCLES / 1024 over GRBM_GUI_ACTIVE / 8", "GRBM_GUI_ACTIVE / 8 over each dispatch's duration")
+
     out = {
         "metric": "attention fwd+bwd TFLOP/s (bf16) and % of MI355X bf16 MFMA peak",
         "value": round(value, 2),
@@ -757,6 +780,7 @@ def main():
                         "share": round(v["share"], 4)} for k, v in kt.items()},
         "roofline": roofline,
         "mfma_busy": mfma_busy,
+        "engine_clock": engine_clock,
         "hbm_step": hbm_step,
         "device_peak_bf16": {"value": device_peak_bf16_tflops(), "unit": "TFLOP/s",
                              "note": "reported peak engine clock x CUs x 4096 flop/clk/CU"},

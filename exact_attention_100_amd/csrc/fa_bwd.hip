@@ -1122,11 +1122,11 @@ void bwd_dkdv_pp_kernel(BwdKParams p) {
     // The last dV, dK products (tile n_qt - 1, in buffer (n_qt - 1) % 3).
     {
       const int jl = (n_qt - 1) % 3;
-      const int qol = jl == 0 ? qbuf(0) : (jl == 1 ? qbuf(1) : qbuf(2));
-      const int dol = jl == 0 ? dobuf(0) : (jl == 1 ? dobuf(1) : dobuf(2));
+      const uint32_t qol = jl == 0 ? qbuf(0) : (jl == 1 ? qbuf(1) : qbuf(2));
+      const uint32_t dol = jl == 0 ? dobuf(0) : (jl == 1 ? dobuf(1) : dobuf(2));
 #pragma unroll
       for (int i = 0; i < NVM; ++i) {
-        const bf16x8 a = ta.read_tr(dol, i / NDB, i % NDB);
+        const bf16x8 a = ta.read_tr_rt(dol, i / NDB, i % NDB);
         lds_wait(0);
         __builtin_amdgcn_sched_barrier(0);
         dvacc[i % NDB] = mfma_bf16(a, pb[i / NDB], dvacc[i % NDB]);
@@ -1134,7 +1134,7 @@ void bwd_dkdv_pp_kernel(BwdKParams p) {
       }
 #pragma unroll
       for (int i = 0; i < NVM; ++i) {
-        const bf16x8 a = ta.read_tr(qol, i / NDB, i % NDB);
+        const bf16x8 a = ta.read_tr_rt(qol, i / NDB, i % NDB);
         lds_wait(0);
         __builtin_amdgcn_sched_barrier(0);
         dkacc[i % NDB] = mfma_bf16(a, dsb[i / NDB], dkacc[i % NDB]);
@@ -1382,15 +1382,15 @@ void bwd_dq_pp_kernel(BwdKParams p) {
     // The last dQ products (tile nt - 1, its K in buffer (nt - 1) % 3).
     {
       const int kl = (nt - 1) % 3;
-      const int klast = kl == 0 ? kbuf(0) : (kl == 1 ? kbuf(1) : kbuf(2));
+      const uint32_t klast = kl == 0 ? kbuf(0) : (kl == 1 ? kbuf(1) : kbuf(2));
       constexpr int AH = 2;
-      bf16x8 a0 = ta.read_tr(klast, 0, 0);
-      bf16x8 a1 = ta.read_tr(klast, 1 / NDB, 1 % NDB);
+      bf16x8 a0 = ta.read_tr_rt(klast, 0, 0);
+      bf16x8 a1 = ta.read_tr_rt(klast, 1 / NDB, 1 % NDB);
 #pragma unroll
       for (int i = 0; i < NQM; ++i) {
         const bf16x8 a = a0;
         a0 = a1;
-        if (i + AH < NQM) a1 = ta.read_tr(klast, (i + AH) / NDB, (i + AH) % NDB);
+        if (i + AH < NQM) a1 = ta.read_tr_rt(klast, (i + AH) / NDB, (i + AH) % NDB);
         lds_wait(2 * ((i + AH < NQM ? i + AH : NQM - 1) - i));
         __builtin_amdgcn_sched_barrier(0);
         dqacc[i % NDB] = mfma_bf16(a, dsb[i / NDB], dqacc[i % NDB]);

@@ -365,6 +365,13 @@ struct TileAddr {
     return concat_bf16x4(lds_read_tr_asm(tr_lo[mb], buf + 32 * ks * COLS),
                          lds_read_tr_asm(tr_hi[mb], buf + 32 * ks * COLS));
   }
+  // The same read from a buffer chosen at run time: its offset goes into the
+  // address (one add per read) and the immediate keeps only the constant part,
+  // where read_tr would branch over the possible immediates.
+  __device__ __forceinline__ bf16x8 read_tr_rt(uint32_t buf, int ks, int mb) const {
+    return concat_bf16x4(lds_read_tr_asm(tr_lo[mb] + buf, 32 * ks * COLS),
+                         lds_read_tr_asm(tr_hi[mb] + buf, 32 * ks * COLS));
+  }
 };
 
 // Dropout keep bits from Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel

@@ -180,7 +180,7 @@ __device__ __forceinline__ float softmax_tile_bf16(f32x16 (&s)[NKB], float c, fl
 #pragma unroll
       for (int i = 8 * sh; i < 8 * sh + 8; ++i) {
         s[kb][i] = fast_exp2(fmaf(s[kb][i], c, -m_use));
-        ru[i & 3] += s[kb][i];
+        ru[i & 3] = (kb == 0 && i < 4) ? s[kb][i] : ru[i & 3] + s[kb][i];  // (0 + x = x for x >= 0)
       }
       pb[2 * kb + sh] = pack_bf16x8(s[kb][8 * sh + 0], s[kb][8 * sh + 1], s[kb][8 * sh + 2], s[kb][8 * sh + 3],
                                     s[kb][8 * sh + 4], s[kb][8 * sh + 5], s[kb][8 * sh + 6], s[kb][8 * sh + 7]);
@@ -398,7 +398,7 @@ void fwd_bf16_kernel(FwdKParams p) {
 #pragma unroll
           for (int e = s0; e < s1; ++e) {
             sacc[e / 16][e % 16] = fast_exp2(fmaf(sacc[e / 16][e % 16], p.c, -m_use));
-            rup[e & 3] += sacc[e / 16][e % 16];
+            rup[e & 3] = e < 4 ? sacc[e / 16][e % 16] : rup[e & 3] + sacc[e / 16][e % 16];
             if ((e & 7) == 7) {  // a group of 8 probabilities is complete: pack and sum it
               const int kb = e / 16, s8 = (e % 16) / 8;
               pbn[2 * kb + s8] = pack_bf16x8(sacc[kb][8 * s8 + 0], sacc[kb][8 * s8 + 1], sacc[kb][8 * s8 + 2],
@@ -590,18 +590,12 @@ void fwd_pp_kernel(FwdKParams p) {
   // packing into pb, and the rescale of O when a row's reference point moved.
   auto softmax = [&](int kv0) __attribute__((always_inline)) {
     if ((kv0 + BC > kv_len) || (p.causal && kv0 + BC - 1 > wrow0)) mask_tile<NKB>(sacc, kv0, kv_len, p.causal, qrow, g);
-    float t8[NE / 4];
+    // (four running maxima: chains the compiler turns into v_max3 without
+    // canonicalising every score first, as it does for a pairwise tree)
+    float t4[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
 #pragma unroll
-    for (int i = 0; i < NE / 4; ++i) {
-      const int e = 4 * i;
-      t8[i] = fmaxf(fmaxf(sacc[e / 16][e % 16], sacc[e / 16][e % 16 + 1]),
-                    fmaxf(sacc[e / 16][e % 16 + 2], sacc[e / 16][e % 16 + 3]));
-    }
-#pragma unroll
-    for (int w = NE / 8; w >= 1; w /= 2)
-#pragma unroll
-      for (int i = 0; i < w; ++i) t8[i] = fmaxf(t8[i], t8[i + w]);
-    const float mx = pair_max(t8[0]);
+    for (int e = 0; e < NE; ++e) t4[(e / 8) & 3] = fmaxf(t4[(e / 8) & 3], sacc[e / 16][e % 16]);
+    const float mx = pair_max(fmaxf(fmaxf(t4[0], t4[1]), fmaxf(t4[2], t4[3])));
     const float mxs = (mx == kNegInf) ? kNegInf : mx * p.c;
     const float m_new = (mxs > m_run + kRescaleSlack) ? mxs : m_run;
     const float m_use = (m_new == kNegInf) ? 0.f : m_new;
@@ -610,7 +604,7 @@ void fwd_pp_kernel(FwdKParams p) {
 #pragma unroll
     for (int e = 0; e < NE; ++e) {
       sacc[e / 16][e % 16] = fast_exp2(fmaf(sacc[e / 16][e % 16], p.c, -m_use));
-      ru[e & 3] += sacc[e / 16][e % 16];
+      ru[e & 3] = e < 4 ? sacc[e / 16][e % 16] : ru[e & 3] + sacc[e / 16][e % 16];  // (0 + x = x for x >= 0)
     }
 #pragma unroll
     for (int k = 0; k < 2 * NKB; ++k) {
@@ -672,16 +666,17 @@ void fwd_pp_kernel(FwdKParams p) {
       if (t + 1 < nt) tile(t + 1, KB0, KB1, VB0, VB1);
     }
     // The last P V (tile nt - 1, its V in buffer (nt - 1) % 2).
-    const int vlast = ((nt - 1) & 1) ? VB1 : VB0;
+    const uint32_t vlast = ((nt - 1) & 1) ? VB1 : VB0;
+    auto read_last = [&](int ks, int db) __attribute__((always_inline)) { return ta.read_tr_rt(vlast, ks, db); };
     {
       constexpr int AH = 2;
-      bf16x8 a0 = ta.read_tr(vlast, 0, 0);
-      bf16x8 a1 = ta.read_tr(vlast, 1 / NDB, 1 % NDB);
+      bf16x8 a0 = read_last(0, 0);
+      bf16x8 a1 = read_last(1 / NDB, 1 % NDB);
 #pragma unroll
       for (int i = 0; i < NPV; ++i) {
         const bf16x8 a = a0;
         a0 = a1;
-        if (i + AH < NPV) a1 = ta.read_tr(vlast, (i + AH) / NDB, (i + AH) % NDB);
+        if (i + AH < NPV) a1 = read_last((i + AH) / NDB, (i + AH) % NDB);
         lds_wait(2 * ((i + AH < NPV ? i + AH : NPV - 1) - i));
         __builtin_amdgcn_sched_barrier(0);
         oacc[i % NDB] = mfma_bf16(a, pb[i / NDB], oacc[i % NDB]);
