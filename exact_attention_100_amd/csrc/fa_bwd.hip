@@ -1010,40 +1010,52 @@ void bwd_dkdv_pp_kernel(BwdKParams p) {
 
     f32x16 sacc, dpacc;
     bf16x8 pb[2], dsb[2];
+    // Operand ring of the product phases (slot m % (AH + 1) holds product m's operands).
+    // A phase's first AH reads are issued at the end of the element phase before it (PRE):
+    // they read the previous tile's dO, resident since that tile's own products, and
+    // arrive while the waves wait at the barrier instead of after it.
+    constexpr int AH = FA_BWD_DKDV_PP_AHEAD;
+    bf16x8 ra[AH + 1], rb[AH + 1];
+    // Issues the LDS reads of product m of a phase over buffers j (this tile) and jp (the
+    // previous one); returns how many reads that is.
+    auto fetch_op = [&](int m, int j, int jp, auto dkv_flag, bool issue) __attribute__((always_inline)) {
+      constexpr bool DKV = decltype(dkv_flag)::value;
+      constexpr int NP = DKV ? 2 * NVM : 0;
+      const int sl = m % (AH + 1);
+      if (m < NP) {
+        const int i = m % NVM;
+        if (issue) ra[sl] = ta.read_tr(m < NVM ? dobuf(jp) : qbuf(jp), i / NDB, i % NDB);
+        return 2;
+      } else if (m < NP + NSM) {
+        if (issue) ra[sl] = ta.read_row(qbuf(j), 0, m - NP);
+        return 1;
+      } else {
+        const int jj = m - NP - NSM;
+        if (issue) {
+          ra[sl] = ta.read_row(dobuf(j), 0, jj);
+          rb[sl] = lds_read_b128_asm(ta.row[jj] + vdelta, 0);
+        }
+        return 2;
+      }
+    };
     // Product phase: (DKV) dV, dK of the previous tile from buffer jp, then S, dP of this
     // tile from buffer j. Every LDS operand is an inline-assembly read issued AH products
     // ahead and waited for exactly.
-    auto products = [&](int j, int jp, auto dkv_flag) __attribute__((always_inline)) {
-      constexpr bool DKV = decltype(dkv_flag)::value;
+    auto products = [&](int j, int jp, auto dkv_flag, auto pre_flag) __attribute__((always_inline)) {
+      constexpr bool DKV = decltype(dkv_flag)::value, PRE = decltype(pre_flag)::value;
       constexpr int NP = DKV ? 2 * NVM : 0;
-      constexpr int NM = NP + 2 * NSM, AH = FA_BWD_DKDV_PP_AHEAD;
-      const int qo = qbuf(j), doo = dobuf(j), qop = qbuf(jp), doop = dobuf(jp);
-      bf16x8 ra[AH + 1], rb[AH + 1];
+      constexpr int NM = NP + 2 * NSM;
       int ia[AH + 1];
       int nrd = 0;
-      auto fetch = [&](int m) __attribute__((always_inline)) {
-        const int sl = m % (AH + 1);
-        if (m < NP) {
-          const int i = m % NVM;
-          ra[sl] = ta.read_tr(m < NVM ? doop : qop, i / NDB, i % NDB);
-          nrd += 2;
-        } else if (m < NP + NSM) {
-          const int jj = m - NP;
-          ra[sl] = ta.read_row(qo, 0, jj);
-          nrd += 1;
-        } else {
-          const int jj = m - NP - NSM;
-          ra[sl] = ta.read_row(doo, 0, jj);
-          rb[sl] = lds_read_b128_asm(ta.row[jj] + vdelta, 0);
-          nrd += 2;
-        }
-        ia[sl] = nrd - 1;
+      auto fetch = [&](int m, bool issue) __attribute__((always_inline)) {
+        nrd += fetch_op(m, j, jp, dkv_flag, issue);
+        ia[m % (AH + 1)] = nrd - 1;
       };
 #pragma unroll
-      for (int m = 0; m < AH; ++m) fetch(m);
+      for (int m = 0; m < AH; ++m) fetch(m, !PRE);
       static_for<NM>([&](auto mc) __attribute__((always_inline)) {
         constexpr int m = decltype(mc)::value;
-        if (m + AH < NM) fetch(m + AH);
+        if (m + AH < NM) fetch(m + AH, true);
         lds_wait(nrd - 1 - ia[m % (AH + 1)]);
         __builtin_amdgcn_sched_barrier(0);
         const bf16x8 a = ra[m % (AH + 1)];
@@ -1107,9 +1119,13 @@ void bwd_dkdv_pp_kernel(BwdKParams p) {
     auto tile = [&](int t, int j, auto dkv_flag) __attribute__((always_inline)) {
       // tile t in buffer j, tile t - 1 in (j + 2) % 3; tile t + 1 goes to (j + 1) % 3
       if (gr == 0) issue_tile(t + 1, (j + 1) % 3);
-      products(j, (j + 2) % 3, dkv_flag);
+      products(j, (j + 2) % 3, dkv_flag, dkv_flag);  // (tiles after the first were prefetched)
       __syncthreads();
       elements(t, j);
+      if (t + 1 < n_qt) {
+#pragma unroll
+        for (int m = 0; m < AH; ++m) fetch_op(m, (j + 1) % 3, j, Flag<true>{}, true);
+      }
       if (gr == 0) wait_vmem();
       __syncthreads();
     };
@@ -1124,20 +1140,22 @@ void bwd_dkdv_pp_kernel(BwdKParams p) {
       const int jl = (n_qt - 1) % 3;
       const uint32_t qol = jl == 0 ? qbuf(0) : (jl == 1 ? qbuf(1) : qbuf(2));
       const uint32_t dol = jl == 0 ? dobuf(0) : (jl == 1 ? dobuf(1) : dobuf(2));
+      // (dV from dO^T, then dK from Q^T; each operand two reads, issued two products ahead)
+      auto rd = [&](int m) __attribute__((always_inline)) {
+        const int i = m % NVM;
+        return ta.read_tr_rt(m < NVM ? dol : qol, i / NDB, i % NDB);
+      };
+      constexpr int NL = 2 * NVM;
+      bf16x8 a0 = rd(0), a1 = rd(1);
 #pragma unroll
-      for (int i = 0; i < NVM; ++i) {
-        const bf16x8 a = ta.read_tr_rt(dol, i / NDB, i % NDB);
-        lds_wait(0);
+      for (int m = 0; m < NL; ++m) {
+        const bf16x8 a = a0;
+        a0 = a1;
+        if (m + 2 < NL) a1 = rd(m + 2);
+        lds_wait(2 * ((m + 2 < NL ? m + 2 : NL - 1) - m));
         __builtin_amdgcn_sched_barrier(0);
-        dvacc[i % NDB] = mfma_bf16(a, pb[i / NDB], dvacc[i % NDB]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-#pragma unroll
-      for (int i = 0; i < NVM; ++i) {
-        const bf16x8 a = ta.read_tr_rt(qol, i / NDB, i % NDB);
-        lds_wait(0);
-        __builtin_amdgcn_sched_barrier(0);
-        dkacc[i % NDB] = mfma_bf16(a, dsb[i / NDB], dkacc[i % NDB]);
+        if (m < NVM) dvacc[m % NDB] = mfma_bf16(a, pb[m / NDB], dvacc[m % NDB]);
+        else dkacc[(m - NVM) % NDB] = mfma_bf16(a, dsb[(m - NVM) / NDB], dkacc[(m - NVM) % NDB]);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -1268,37 +1286,47 @@ void bwd_dq_pp_kernel(BwdKParams p) {
   f32x16 sacc[NKB], dpacc[NKB];
   bf16x8 dsb[2 * NKB];
 
+  // Operand ring of the product phases (slot m % (AH + 1) holds product m's operand). A
+  // phase's first AH reads are issued at the end of the element phase before it (PRE):
+  // they read K_{t-1}, resident since that tile's own products, and arrive while the
+  // waves wait at the barrier instead of after it.
+  constexpr int AH = FA_BWD_DQ_PP_AHEAD;
+  bf16x8 ra[AH + 1];
+  // Issues the LDS reads of product m of a phase (buffers kp, kb, vb); returns their number.
+  auto fetch_op = [&](int m, int kp, int kb, int vb, auto dq_flag, bool issue) __attribute__((always_inline)) {
+    constexpr int NQ = decltype(dq_flag)::value ? NQM : 0;
+    const int sl = m % (AH + 1);
+    if (m < NQ) {
+      if (issue) ra[sl] = ta.read_tr(kp, m / NDB, m % NDB);
+      return 2;
+    } else if (m < NQ + NS) {
+      const int j = m - NQ;
+      if (issue) ra[sl] = ta.read_row(kb, j / NKK, j % NKK);
+      return 1;
+    } else {
+      const int j = m - NQ - NS;
+      if (issue) ra[sl] = ta.read_row(vb, j / NKK, j % NKK);
+      return 1;
+    }
+  };
   // Product phase: (DQ) dQ^T += K_{t-1}^T dS^T(t - 1) from the K buffer at kp, then
   // S^T(t) and dP^T(t) from the K / V buffers at kb / vb. LDS operands are inline-
   // assembly reads issued AH products ahead and waited for exactly.
-  auto products = [&](int kp, int kb, int vb, auto dq_flag) __attribute__((always_inline)) {
-    constexpr bool DQ = decltype(dq_flag)::value;
+  auto products = [&](int kp, int kb, int vb, auto dq_flag, auto pre_flag) __attribute__((always_inline)) {
+    constexpr bool DQ = decltype(dq_flag)::value, PRE = decltype(pre_flag)::value;
     constexpr int NQ = DQ ? NQM : 0;
-    constexpr int NM = NQ + 2 * NS, AH = FA_BWD_DQ_PP_AHEAD;
-    bf16x8 ra[AH + 1];
+    constexpr int NM = NQ + 2 * NS;
     int ia[AH + 1];
     int nrd = 0;
-    auto fetch = [&](int m) __attribute__((always_inline)) {
-      const int sl = m % (AH + 1);
-      if (m < NQ) {
-        ra[sl] = ta.read_tr(kp, m / NDB, m % NDB);
-        nrd += 2;
-      } else if (m < NQ + NS) {
-        const int j = m - NQ;
-        ra[sl] = ta.read_row(kb, j / NKK, j % NKK);
-        nrd += 1;
-      } else {
-        const int j = m - NQ - NS;
-        ra[sl] = ta.read_row(vb, j / NKK, j % NKK);
-        nrd += 1;
-      }
-      ia[sl] = nrd - 1;
+    auto fetch = [&](int m, bool issue) __attribute__((always_inline)) {
+      nrd += fetch_op(m, kp, kb, vb, dq_flag, issue);
+      ia[m % (AH + 1)] = nrd - 1;
     };
 #pragma unroll
-    for (int m = 0; m < AH && m < NM; ++m) fetch(m);
+    for (int m = 0; m < AH && m < NM; ++m) fetch(m, !PRE);
     static_for<NM>([&](auto mc) __attribute__((always_inline)) {
       constexpr int m = decltype(mc)::value;
-      if (m + AH < NM) fetch(m + AH);
+      if (m + AH < NM) fetch(m + AH, true);
       lds_wait(nrd - 1 - ia[m % (AH + 1)]);
       __builtin_amdgcn_sched_barrier(0);
       const bf16x8 a = ra[m % (AH + 1)];
@@ -1362,9 +1390,13 @@ void bwd_dq_pp_kernel(BwdKParams p) {
         cp.issue(sT + kbuf((jk + 1) % 3) / 2, Kh, p.sn, kv0_of(t + 1), N);
         cp.issue(sT + vbuf(1 - jv) / 2, Vh, p.sn, kv0_of(t + 1), N);
       }
-      products(kbuf((jk + 2) % 3), kbuf(jk), vbuf(jv), dq_flag);
+      products(kbuf((jk + 2) % 3), kbuf(jk), vbuf(jv), dq_flag, dq_flag);  // (tiles after the first were prefetched)
       __syncthreads();
       elements(kv0_of(t));
+      if (t + 1 < nt) {
+#pragma unroll
+        for (int m = 0; m < AH; ++m) fetch_op(m, kbuf(jk), kbuf((jk + 1) % 3), vbuf(1 - jv), Flag<true>{}, true);
+      }
       if (gr == 0) wait_vmem();
       __syncthreads();
     };
