@@ -172,6 +172,42 @@ def sq_digest(p1: str, p2: str, workload: str):
     return out, "\n".join(lines)
 
 
+# LDS counters (one rocprofv3 --pmc run): latency, bytes delivered, FIFO stalls, MFMA / VALU co-execution.
+LDS_SET = ["LdsLatency", "SQ_LDS_IDX_ACTIVE", "SQ_LDS_CMD_FIFO_FULL", "SQ_LDS_DATA_FIFO_FULL",
+           "SQ_VALU_MFMA_COEXEC_CYCLES", "SQ_INSTS_LDS_LOAD_BANDWIDTH", "GRBM_GUI_ACTIVE"]
+
+
+def digest_lds(p: str, workload: str):
+    """Per-kernel LDS summary of one rocprofv3 --pmc csv run over LDS_SET: the mean LDS latency, the LDS bytes
+    loaded per compute-unit cycle (SQ_INSTS_LDS_LOAD_BANDWIDTH counts 64-byte units over the 256 CUs), the share
+    of CU cycles with the LDS command FIFO full, the share of SIMD cycles in which a VALU instruction issued while
+    the matrix core was busy, and the engine clock (GRBM_GUI_ACTIVE / 8 over the dispatch's duration)."""
+    import csv
+    import glob
+    import re
+    vals, durs = {}, {}
+    for f in glob.glob(os.path.join(p, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for row in csv.DictReader(fh):
+                k = re.sub(r"^void fa::", "", row["Kernel_Name"]).split("(")[0]
+                vals.setdefault(k, {}).setdefault(row["Counter_Name"], []).append(float(row["Counter_Value"]))
+                if row["Counter_Name"] == "GRBM_GUI_ACTIVE":
+                    durs.setdefault(k, []).append(int(row["End_Timestamp"]) - int(row["Start_Timestamp"]))
+    print(f"workload {workload}, kernel sources_hash {sources_hash()}")
+    for k, cs in vals.items():
+        if not any(frag in k for frag in KERNEL_NAMES):
+            continue
+        m = {c: sum(v) / len(v) for c, v in cs.items()}
+        cyc = m["GRBM_GUI_ACTIVE"] / 8  # engine cycles per XCD
+        print(k, f"({len(durs.get(k, []))} dispatches)")
+        print("  " + "  ".join(f"{c}={m[c]:.4g}" for c in sorted(m)))
+        print(f"  LDS latency {m['LdsLatency']:.1f} cycles; LDS bytes loaded per CU-cycle "
+              f"{m['SQ_INSTS_LDS_LOAD_BANDWIDTH'] * 64 / 256 / cyc:.1f}; LDS command FIFO full "
+              f"{100 * m['SQ_LDS_CMD_FIFO_FULL'] / 256 / cyc:.2f}% of CU-cycles; VALU issued beside a busy matrix "
+              f"core {100 * m['SQ_VALU_MFMA_COEXEC_CYCLES'] / 1024 / cyc:.1f}% of SIMD-cycles; engine clock "
+              f"{cyc / (sum(durs[k]) / len(durs[k])) * 1e3:.0f} MHz", flush=True)
+
+
 def digest_sq(p1: str, p2: str, workload: str):
     """Prints sq_digest's text and the JSON that bench.py reads from profiles/."""
     rec, text = sq_digest(p1, p2, workload)
@@ -588,6 +624,8 @@ def main():
                          "runs on this box (falls back to the committed digests if that fails)")
     ap.add_argument("--digest-sq", nargs=2, metavar=("P1_DIR", "P2_DIR"),
                     help="print per-kernel SQ counter summaries from two rocprofv3 --pmc csv runs")
+    ap.add_argument("--digest-lds", metavar="DIR",
+                    help="print per-kernel LDS counter summaries from one rocprofv3 --pmc csv run over LDS_SET")
     ap.add_argument("--memory-sweep", nargs="*", type=int, metavar="N",
                     help="peak memory and time of this path and of standard attention over N "
                          "(B=1, H=16, d=64; default N = 128 .. 64K)")
@@ -603,6 +641,9 @@ def main():
         return
     if args.digest_sq:
         digest_sq(*args.digest_sq, workload=args.workload)
+        return
+    if args.digest_lds:
+        digest_lds(args.digest_lds, workload=args.workload)
         return
     if args.calibrate_copy:
         calibrate_copy()
