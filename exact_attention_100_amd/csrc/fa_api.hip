@@ -119,9 +119,10 @@ int check_desc(const fa_desc* d) {
   const int64_t align = 16 / (int64_t)elem_bytes(d->dtype);
   if (d->stride_n < d->d || d->stride_h < 1 || d->stride_b < 1) return FA_ERR_INVALID;
   if (d->stride_n % align || d->stride_h % align || d->stride_b % align) return FA_ERR_INVALID;
-  // The tile copies keep each lane's offset from a tile's first row (up to 128 rows)
-  // in 32 bits: 128 stride_n must stay below 2^31.
-  if (d->stride_n >= ((int64_t)1 << 24)) return FA_ERR_UNSUPPORTED;
+  // The tile copies keep each lane's offset from a tile's first row in 32 bits, and the
+  // largest tile has 256 rows (the dK/dV pass's resident V block): 256 stride_n must
+  // stay below 2^31.
+  if (d->stride_n >= ((int64_t)1 << 23)) return FA_ERR_UNSUPPORTED;
   // The largest element offset, (B-1) stride_b + (H-1) stride_h + (N-1) stride_n + d, must
   // be an address a device can hold (2^48 elements): the kernels form it in 64 bits.
   int64_t span = d->d, part = 0;

@@ -160,6 +160,8 @@ struct TileCopy {
   static constexpr int CPR = COLS / 8;
   static constexpr int PER_WAVE = ROWS * CPR / (64 * NWAVES);
   static_assert(PER_WAVE >= 1 && PER_WAVE * 64 * NWAVES == ROWS * CPR, "tile must split into whole wave copies");
+  // Row offsets are 32-bit: the API admits row strides below 2^23 elements, so 256 rows at most.
+  static_assert(ROWS <= 256, "32-bit lane offsets cover 256 rows of the largest admitted stride");
   int32_t off[PER_WAVE];  // element offset of this lane's source chunk from the tile's first row
   int32_t row[PER_WAVE];  // tile row of that chunk
   int wave;               // wave index (uniform)

@@ -77,8 +77,8 @@ typedef struct fa_desc {
   int32_t dtype;      /* FA_BF16 or FA_F32 */
   int32_t reserved;   /* must be 0 */
   int64_t stride_b, stride_h, stride_n; /* element strides; the d stride is 1. stride_n
-                          must be below 2^24 elements (FA_ERR_UNSUPPORTED otherwise: the
-                          tile copies form a lane's offset within 128 rows in 32 bits) */
+                          must be below 2^23 elements (FA_ERR_UNSUPPORTED otherwise: the
+                          tile copies form a lane's offset within 256 rows in 32 bits) */
 } fa_desc;
 
 /* Forward: O = softmax(scale * Q K^T + mask) V and LSE (see above).

@@ -88,18 +88,18 @@ int main() {
   heads.stride_h = 128 * 64;
   heads.stride_b = int64_t{128} * 64 << 16;
   expect("fwd 2^32 instances", fa_fwd(&heads, A, A, A, 0.1f, 0, nullptr, A, F, nullptr), FA_ERR_UNSUPPORTED);
-  // Row strides at the tile copies' 32-bit limit: 2^24 - 8 elements passes the descriptor
-  // checks (the null Q is what is rejected), 2^24 does not.
+  // Row strides at the tile copies' 32-bit limit (256-row tiles): 2^23 - 8 elements passes
+  // the descriptor checks (the null Q is what is rejected), 2^23 does not.
   fa_desc rs = desc(2, 3, 256, 64);
-  rs.stride_n = (int64_t{1} << 24) - 8;
+  rs.stride_n = (int64_t{1} << 23) - 8;
   rs.stride_h = rs.stride_n * 256;
   rs.stride_b = rs.stride_h * 3;
-  expect("fwd stride_n 2^24 - 8", fa_fwd(&rs, nullptr, A, A, 0.1f, 0, nullptr, A, F, nullptr), FA_ERR_INVALID);
-  rs.stride_n = int64_t{1} << 24;
+  expect("fwd stride_n 2^23 - 8", fa_fwd(&rs, nullptr, A, A, 0.1f, 0, nullptr, A, F, nullptr), FA_ERR_INVALID);
+  rs.stride_n = int64_t{1} << 23;
   rs.stride_h = rs.stride_n * 256;
   rs.stride_b = rs.stride_h * 3;
-  expect("fwd stride_n 2^24", fa_fwd(&rs, A, A, A, 0.1f, 0, nullptr, A, F, nullptr), FA_ERR_UNSUPPORTED);
-  expect("bwd stride_n 2^24", fa_bwd(&rs, A, A, A, A, A, F, 0.1f, 0, nullptr, A, A, A, A, size_t{1} << 40, nullptr),
+  expect("fwd stride_n 2^23", fa_fwd(&rs, A, A, A, 0.1f, 0, nullptr, A, F, nullptr), FA_ERR_UNSUPPORTED);
+  expect("bwd stride_n 2^23", fa_bwd(&rs, A, A, A, A, A, F, 0.1f, 0, nullptr, A, A, A, A, size_t{1} << 40, nullptr),
          FA_ERR_UNSUPPORTED);
   const fa_desc d96 = desc(2, 3, 256, 96);
   expect("fwd d=96", fa_fwd(&d96, A, A, A, 0.1f, 0, nullptr, A, F, nullptr), FA_ERR_UNSUPPORTED);

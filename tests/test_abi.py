@@ -67,6 +67,14 @@ def test_argument_errors_before_any_launch(lib):
     odd = _desc()
     odd.stride_n = 65  # row stride not a multiple of 16 bytes
     assert lib.fa_fwd(ref(odd), A, A, A, 0.1, 0, None, A, A, None) == -1
+    # row strides from 2^23 elements on are refused (32-bit lane offsets over 256-row tiles);
+    # just below the limit the descriptor passes and the null output is what is refused
+    wide = _desc(B=1, H=1)
+    wide.stride_n = wide.stride_h = wide.stride_b = 1 << 23
+    assert lib.fa_fwd(ref(wide), A, A, A, 0.1, 0, None, A, A, None) == -2
+    assert lib.fa_bwd(ref(wide), A, A, A, A, A, A, 0.1, 0, None, A, A, A, A, 1 << 30, None) == -2
+    wide.stride_n = (1 << 23) - 16
+    assert lib.fa_fwd(ref(wide), A, A, A, 0.1, 0, None, None, A, None) == -1
     # backward: fp32 unsupported, workspace checks
     assert lib.fa_bwd(ref(_desc(dtype=1)), A, A, A, A, A, A, 0.1, 0, None, A, A, A, A, 1 << 30, None) == -2
     need = lib.fa_bwd_workspace_bytes(ref(d))
