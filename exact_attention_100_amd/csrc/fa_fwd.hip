@@ -135,32 +135,39 @@ __device__ __forceinline__ float online_softmax_step(f32x16 (&s)[NKB], float c, 
 
 // ----------------------------------------------------------------------------------- bf16
 
-// Adds the 8 bf16 values of one packed operand to four partial sums (v_dot2 against
-// ones), one per 32-bit word (word i into acc[i]); the bf16 kernels combine them as
-// (acc0 + acc1) + (acc2 + acc3). (Through a scalar copy: this compiler's
-// __builtin_bit_cast of a vector element expression reads element 0 whatever the index.)
-__device__ __forceinline__ void sum_bf16x8_4(bf16x8 v, float (&acc)[4]) {
-  const u32x4 u = __builtin_bit_cast(u32x4, v);
-  const bf16x2 one = {(bf16)1.f, (bf16)1.f};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t w = u[i];
-    acc[i] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), one, acc[i], false);
-  }
-}
 __device__ __forceinline__ float sum4(const float (&acc)[4]) { return (acc[0] + acc[1]) + (acc[2] + acc[3]); }
+
+// O's normaliser, the row sum of the bf16-rounded probabilities, on the matrix cores:
+// one 16x16x32 product per packed P^T operand pb (lane l: 8 probabilities of query
+// l % 32). That product reads lane l's 8 values as k-slots 8 (l / 16) .. + 7 of column
+// l % 16, so a column's slots come from lanes n, n + 32 (query n) and n + 16, n + 48
+// (query n + 16). The A operand below (rowsum_selector) is 1 in rows i whose i / 4 has
+// the parity of the slot group and 0 elsewhere: output rows 4 (l / 16) .. + 3 of column
+// l % 16, the four registers lane l receives, then all hold the sum of the operand's 16
+// probabilities of lane l's own query. Each product replaces 4 v_dot2 (the VALU
+// instruction that slows most beside another wave's products) with 16 matrix-core cycles.
+__device__ __forceinline__ bf16x8 rowsum_selector(int lane) {
+  const bf16 v = (((lane >> 4) & 1) == (((lane & 15) >> 2) & 1)) ? (bf16)1.f : (bf16)0.f;
+  bf16x8 a;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a[i] = v;
+  return a;
+}
+__device__ __forceinline__ f32x4 rowsum_mfma(bf16x8 sel, bf16x8 pb, f32x4 acc) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel, pb, acc, 0, 0, 0);
+}
 
 // The bf16 kernels' softmax step: as online_softmax_step, but the probabilities
 // are packed to bf16 (pb, the B operands of the P V product; k-step ks = 2 kb + s
-// holds registers 8 s .. 8 s + 7 of block kb) and two row sums are kept. l_run
-// adds up the rounded values: O's normaliser is then the sum of exactly the
-// weights the product applies, so O is a convex combination of V rows and a bf16
-// rounding of a dominant probability cancels instead of scaling O. lu_run adds
-// up the unrounded float32 values, the row sum of exp(S - m) that LSE = m + ln l
-// is defined with (the running sum of the tiled softmax).
+// holds registers 8 s .. 8 s + 7 of block kb) and two row sums are kept. O's
+// normaliser adds up the rounded values (rowsum_mfma over pb, by the caller): it is
+// then the sum of exactly the weights the product applies, so O is a convex
+// combination of V rows and a bf16 rounding of a dominant probability cancels
+// instead of scaling O. lu_run adds up the unrounded float32 values, the row sum of
+// exp(S - m) that LSE = m + ln l is defined with (the running sum of the tiled softmax).
 template <int NKB>
-__device__ __forceinline__ float softmax_tile_bf16(f32x16 (&s)[NKB], float c, float& m_run, float& l_run,
-                                                   float& lu_run, bf16x8 (&pb)[2 * NKB]) {
+__device__ __forceinline__ float softmax_tile_bf16(f32x16 (&s)[NKB], float c, float& m_run, float& lu_run,
+                                                   bf16x8 (&pb)[2 * NKB]) {
   float mx = kNegInf;
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb)
@@ -172,7 +179,7 @@ __device__ __forceinline__ float softmax_tile_bf16(f32x16 (&s)[NKB], float c, fl
   const float m_use = (m_new == kNegInf) ? 0.f : m_new;
   const float alpha = fast_exp2(m_run - m_use);
   m_run = m_new;
-  float rs[4] = {0.f, 0.f, 0.f, 0.f}, ru[4] = {0.f, 0.f, 0.f, 0.f};
+  float ru[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -184,9 +191,7 @@ __device__ __forceinline__ float softmax_tile_bf16(f32x16 (&s)[NKB], float c, fl
       }
       pb[2 * kb + sh] = pack_bf16x8(s[kb][8 * sh + 0], s[kb][8 * sh + 1], s[kb][8 * sh + 2], s[kb][8 * sh + 3],
                                     s[kb][8 * sh + 4], s[kb][8 * sh + 5], s[kb][8 * sh + 6], s[kb][8 * sh + 7]);
-      sum_bf16x8_4(pb[2 * kb + sh], rs);
     }
-  l_run = l_run * alpha + sum4(rs);
   lu_run = lu_run * alpha + sum4(ru);
   return alpha;
 }
@@ -200,7 +205,7 @@ __device__ __forceinline__ float softmax_tile_bf16(f32x16 (&s)[NKB], float c, fl
 // SMASK: a block-sparse launch that also applies the causal / key-length
 // element masks (without it, sparse tiles are never masked). DROP: dropout on P
 // (dense and block-sparse launches): dropped entries of the packed bf16
-// probabilities are zeroed after their row sums are taken, and O is scaled by
+// probabilities are zeroed after both row sums have taken them, and O is scaled by
 // 1 / (1 - p) at the end.
 template <int D, int BC, bool SPARSE, bool SMASK = false, bool DROP = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FA_FWD_WAVES_PER_EU)))
@@ -256,7 +261,9 @@ void fwd_bf16_kernel(FwdKParams p) {
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
-  float m_run = kNegInf, l_run = 0.f, lu_run = 0.f;
+  float m_run = kNegInf, lu_run = 0.f;
+  f32x4 lacc = {0.f, 0.f, 0.f, 0.f};  // O's normaliser (rowsum_mfma; every register holds it)
+  const bf16x8 sel = rowsum_selector(lane);
 
   // Software pipeline over the key tiles. Iteration t computes S(t) = K_t Q^T,
   // then the P V product of tile t - 1 interleaved with the softmax of tile t, so
@@ -343,7 +350,9 @@ void fwd_bf16_kernel(FwdKParams p) {
       if (needs_mask(kv0_of(0))) mask_tile<NKB>(sacc, kv0_of(0), rg.kv_len, p.causal, qrow, g);
       // P^T as B operands: k-step ks = 2 kb + s covers keys 32 kb + 16 s +
       // {4g..4g+3, 8+4g..8+4g+3}. (alpha is irrelevant: nothing accumulated yet.)
-      softmax_tile_bf16<NKB>(sacc, p.c, m_run, l_run, lu_run, pb);
+      softmax_tile_bf16<NKB>(sacc, p.c, m_run, lu_run, pb);
+#pragma unroll
+      for (int k = 0; k < 2 * NKB; ++k) lacc = rowsum_mfma(sel, pb[k], lacc);
       if (DROP) drop_tile(pb, kv0_of(0));
     }
     wait_vmem();
@@ -361,7 +370,8 @@ void fwd_bf16_kernel(FwdKParams p) {
       // The P V of tile t - 1 and the softmax of tile t are independent. They are
       // interleaved by hand, one slice of softmax work per P V MFMA (scheduling
       // fences keep the slices in place): slices 0-1 the row max, slice 2 the new
-      // reference point, the rest the exponentials, row sums and bf16 packing.
+      // reference point, the rest the exponentials, the unrounded row sum and bf16
+      // packing; O's normaliser follows as rowsum_mfma products after the slices.
       // The transposing LDS reads of each MFMA's operand run two slices ahead.
       constexpr int NPV = NDB * (BC / 16);
       constexpr int NE = NKB * 16;  // scores per lane
@@ -372,7 +382,7 @@ void fwd_bf16_kernel(FwdKParams p) {
       bf16x8 a0 = ta.read_tr(voff, 0, 0);
       bf16x8 a1 = ta.read_tr(voff, 1 / NDB, 1 % NDB);
       float mx0 = kNegInf, mx1 = kNegInf, m_new = 0.f, m_use = 0.f, alpha = 1.f;
-      float rsp[4] = {0.f, 0.f, 0.f, 0.f}, rup[4] = {0.f, 0.f, 0.f, 0.f};
+      float rup[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int i = 0; i < NPV; ++i) {
         const bf16x8 a = a0;
@@ -399,12 +409,11 @@ void fwd_bf16_kernel(FwdKParams p) {
           for (int e = s0; e < s1; ++e) {
             sacc[e / 16][e % 16] = fast_exp2(fmaf(sacc[e / 16][e % 16], p.c, -m_use));
             rup[e & 3] = e < 4 ? sacc[e / 16][e % 16] : rup[e & 3] + sacc[e / 16][e % 16];
-            if ((e & 7) == 7) {  // a group of 8 probabilities is complete: pack and sum it
+            if ((e & 7) == 7) {  // a group of 8 probabilities is complete: pack it
               const int kb = e / 16, s8 = (e % 16) / 8;
               pbn[2 * kb + s8] = pack_bf16x8(sacc[kb][8 * s8 + 0], sacc[kb][8 * s8 + 1], sacc[kb][8 * s8 + 2],
                                              sacc[kb][8 * s8 + 3], sacc[kb][8 * s8 + 4], sacc[kb][8 * s8 + 5],
                                              sacc[kb][8 * s8 + 6], sacc[kb][8 * s8 + 7]);
-              sum_bf16x8_4(pbn[2 * kb + s8], rsp);
             }
           }
         }
@@ -414,18 +423,21 @@ void fwd_bf16_kernel(FwdKParams p) {
       // rescale branch, out of the slices they were placed in.
 #pragma unroll
       for (int i = 0; i < 2 * NKB; ++i) asm volatile("" : "+v"(pbn[i]));
-      float rs = sum4(rsp), ru = sum4(rup);
-      asm volatile("" : "+v"(rs), "+v"(ru), "+v"(alpha), "+v"(m_new));
-      if (DROP) drop_tile(pbn, kv0);
+      float ru = sum4(rup);
+      asm volatile("" : "+v"(ru), "+v"(alpha), "+v"(m_new));
       const float m_prev = m_run;
       m_run = m_new;
-      l_run = l_run * alpha + rs;
       lu_run = lu_run * alpha + ru;
       // alpha == 1 exactly when no row of this wave moved its reference max.
       if (__builtin_amdgcn_ballot_w64(m_run != m_prev)) {
 #pragma unroll
         for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+        lacc *= alpha;
       }
+      // O's normaliser takes this tile's rounded probabilities before dropout.
+#pragma unroll
+      for (int k = 0; k < 2 * NKB; ++k) lacc = rowsum_mfma(sel, pbn[k], lacc);
+      if (DROP) drop_tile(pbn, kv0);
 #pragma unroll
       for (int i = 0; i < 2 * NKB; ++i) pb[i] = pbn[i];
       wait_vmem();
@@ -442,7 +454,7 @@ void fwd_bf16_kernel(FwdKParams p) {
 
   // Epilogue: O = O_acc / l (the rounded weights' sum), LSE = (m + log2 lu) ln 2 (the
   // unrounded sum). Rows with no key: O = 0, LSE = -inf.
-  const float l_tot = pair_sum(l_run);
+  const float l_tot = lacc[0];
   const float lu_tot = pair_sum(lu_run);
   const float inv = l_tot > 0.f ? (DROP ? p.drop.scale : 1.f) / l_tot : 0.f;
   if (qrow < N) {
@@ -472,8 +484,8 @@ void fwd_bf16_kernel(FwdKParams p) {
 // reads) keeps the matrix core busy while the wave beside it on the SIMD issues its
 // VALU work, so each SIMD overlaps the two kinds of work instead of interleaving them
 // inside one instruction stream. The arithmetic is that of fwd_bf16_kernel in the same
-// order (same products per accumulator, same row-sum chains), so the two kernels give
-// the same bits.
+// order (same products per accumulator, the normaliser's products after each tile's
+// rescale, the same unrounded row-sum chains), so the two kernels give the same bits.
 // Wave (group gr, index wg) owns the 32 rows q0 + 64 wg + 32 gr ..: the two waves of a
 // SIMD see the same key tiles, and both groups visit the same tiles of the diagonal.
 // K/V tiles are double-buffered and copied by group 0 at the start of its product
@@ -530,7 +542,9 @@ void fwd_pp_kernel(FwdKParams p) {
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
-  float m_run = kNegInf, l_run = 0.f, lu_run = 0.f;
+  float m_run = kNegInf, lu_run = 0.f;
+  f32x4 lacc = {0.f, 0.f, 0.f, 0.f};  // O's normaliser (rowsum_mfma; every register holds it)
+  const bf16x8 sel = rowsum_selector(lane);
   f32x16 sacc[NKB];
   bf16x8 pb[2 * NKB];
 
@@ -579,15 +593,17 @@ void fwd_pp_kernel(FwdKParams p) {
       } else {
         constexpr int i = m - NS;
         oacc[i % NDB] = mfma_bf16(a, pb[i / NDB], oacc[i % NDB]);
+        if constexpr (i % NDB == NDB - 1) lacc = rowsum_mfma(sel, pb[i / NDB], lacc);
       }
       __builtin_amdgcn_sched_barrier(0);
     });
   };
 
   // Softmax phase of the tile at kv0: mask (only where the tile needs it), row max,
-  // reference point, exponentials, both row sums (four partial sums each, combined as in
-// fwd_bf16_kernel), bf16
-  // packing into pb, and the rescale of O when a row's reference point moved.
+  // reference point, exponentials, the unrounded row sum (four partial sums, combined as
+  // in fwd_bf16_kernel), bf16 packing into pb, and the rescale of O and of its normaliser
+  // when a row's reference point moved (the normaliser's products for pb run beside the
+  // P V products of the next product phase).
   auto softmax = [&](int kv0) __attribute__((always_inline)) {
     if ((kv0 + BC > kv_len) || (p.causal && kv0 + BC - 1 > wrow0)) mask_tile<NKB>(sacc, kv0, kv_len, p.causal, qrow, g);
     // (four running maxima: chains the compiler turns into v_max3 without
@@ -600,7 +616,7 @@ void fwd_pp_kernel(FwdKParams p) {
     const float m_new = (mxs > m_run + kRescaleSlack) ? mxs : m_run;
     const float m_use = (m_new == kNegInf) ? 0.f : m_new;
     const float alpha = fast_exp2(m_run - m_use);
-    float rs[4] = {0.f, 0.f, 0.f, 0.f}, ru[4] = {0.f, 0.f, 0.f, 0.f};
+    float ru[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int e = 0; e < NE; ++e) {
       sacc[e / 16][e % 16] = fast_exp2(fmaf(sacc[e / 16][e % 16], p.c, -m_use));
@@ -611,20 +627,19 @@ void fwd_pp_kernel(FwdKParams p) {
       const int kb = k / 2, s8 = 8 * (k % 2);
       pb[k] = pack_bf16x8(sacc[kb][s8 + 0], sacc[kb][s8 + 1], sacc[kb][s8 + 2], sacc[kb][s8 + 3], sacc[kb][s8 + 4],
                           sacc[kb][s8 + 5], sacc[kb][s8 + 6], sacc[kb][s8 + 7]);
-      sum_bf16x8_4(pb[k], rs);
     }
     const float m_prev = m_run;
     m_run = m_new;
-    l_run = l_run * alpha + sum4(rs);
     lu_run = lu_run * alpha + sum4(ru);
     if (__builtin_amdgcn_ballot_w64(m_run != m_prev)) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+      lacc *= alpha;
     }
     // (keeps the phase's work inside it: nothing may sink past the barrier's wait)
 #pragma unroll
     for (int k = 0; k < 2 * NKB; ++k) asm volatile("" : "+v"(pb[k]));
-    asm volatile("" : "+v"(l_run), "+v"(lu_run));
+    asm volatile("" : "+v"(lu_run));
   };
 
   // Both groups run the same sequence (product phase t, barrier, softmax phase t,
@@ -680,6 +695,7 @@ void fwd_pp_kernel(FwdKParams p) {
         lds_wait(2 * ((i + AH < NPV ? i + AH : NPV - 1) - i));
         __builtin_amdgcn_sched_barrier(0);
         oacc[i % NDB] = mfma_bf16(a, pb[i / NDB], oacc[i % NDB]);
+        if (i % NDB == NDB - 1) lacc = rowsum_mfma(sel, pb[i / NDB], lacc);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -687,7 +703,7 @@ void fwd_pp_kernel(FwdKParams p) {
   }
 
   // Epilogue: O = O_acc / l (the rounded weights' sum), LSE = (m + log2 lu) ln 2.
-  const float l_tot = pair_sum(l_run);
+  const float l_tot = lacc[0];
   const float lu_tot = pair_sum(lu_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (qrow < N) {
