@@ -381,7 +381,9 @@ void fwd_bf16_kernel(FwdKParams p) {
       const int voff = (int)(lds_address(vr) - lds_address(sT));
       bf16x8 a0 = ta.read_tr(voff, 0, 0);
       bf16x8 a1 = ta.read_tr(voff, 1 / NDB, 1 % NDB);
-      float mx0 = kNegInf, mx1 = kNegInf, m_new = 0.f, m_use = 0.f, alpha = 1.f;
+      // (row max as four running maxima, each slice extending all four: independent
+      // v_max3 chains instead of one dependent chain per slice)
+      float t4[4] = {kNegInf, kNegInf, kNegInf, kNegInf}, m_new = 0.f, m_use = 0.f, alpha = 1.f;
       float rup[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int i = 0; i < NPV; ++i) {
@@ -393,12 +395,12 @@ void fwd_bf16_kernel(FwdKParams p) {
         oacc[i % NDB] = mfma_bf16(a, pb[i / NDB], oacc[i % NDB]);
         if (i == 0) {
 #pragma unroll
-          for (int e = 0; e < NE / 2; ++e) mx0 = fmaxf(mx0, sacc[e / 16][e % 16]);
+          for (int e = 0; e < NE / 2; ++e) t4[(e / 4) & 3] = fmaxf(t4[(e / 4) & 3], sacc[e / 16][e % 16]);
         } else if (i == 1) {
 #pragma unroll
-          for (int e = NE / 2; e < NE; ++e) mx1 = fmaxf(mx1, sacc[e / 16][e % 16]);
+          for (int e = NE / 2; e < NE; ++e) t4[(e / 4) & 3] = fmaxf(t4[(e / 4) & 3], sacc[e / 16][e % 16]);
         } else if (i == 2) {
-          const float mx = pair_max(fmaxf(mx0, mx1));
+          const float mx = pair_max(fmaxf(fmaxf(t4[0], t4[1]), fmaxf(t4[2], t4[3])));
           const float mxs = (mx == kNegInf) ? kNegInf : mx * p.c;
           m_new = (mxs > m_run + kRescaleSlack) ? mxs : m_run;
           m_use = (m_new == kNegInf) ? 0.f : m_new;
