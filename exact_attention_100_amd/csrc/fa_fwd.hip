@@ -90,13 +90,16 @@ __device__ __forceinline__ int fwd_tile_kv0(const FwdKParams& p, const FwdRange&
 // key is past kv_len or, when causal, after the query become -inf.
 template <int NKB>
 __device__ __forceinline__ void mask_tile(f32x16 (&s)[NKB], int kv0, int kv_len, int causal, int qrow, int g) {
+  // Register r of block kb is key kv0 + 4 g + off with off = 32 kb + 8 (r/4) + r%4 a
+  // compile-time constant, kept iff key <= min(kv_len - 1, qrow when causal): one
+  // compare against a constant per entry.
+  const int lim = min(kv_len - 1, causal ? qrow : 0x3FFFFFFF) - kv0 - 4 * g;
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int key = kv0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-      const bool ok = key < kv_len && (!causal || key <= qrow);
-      if (!ok) s[kb][r] = kNegInf;
+      const int off = kb * 32 + 8 * (r >> 2) + (r & 3);
+      if (off > lim) s[kb][r] = kNegInf;
     }
 }
 
