@@ -146,6 +146,10 @@ void bwd_dkdv_kernel(BwdKParams p) {
 
   int kv_len = N;
   if (p.key_len) kv_len = min(max(p.key_len[b], 0), N);
+  // The tile-independent parts of the element mask's bounds (see mask_scores), formed
+  // once per lane so that no per-lane predicate stays live across the tile loop.
+  const int lo_lane = mykey < kv_len ? (p.causal ? mykey : 0) - 4 * g : 0x7FFFFFFF;  // (minus q0 >= 0: no overflow)
+  const int hi_lane = N - 1 - 4 * g;
 
   // The query tiles this key block visits (none when all its keys are past
   // kv_len: dK = dV = 0).
@@ -241,14 +245,13 @@ void bwd_dkdv_kernel(BwdKParams p) {
       // constant: the entry is kept iff lo <= off <= hi (the lane's key is below kv_len
       // and, when causal, at or before the query; the query is below N).
       auto mask_scores = [&](f32x16 (&s)[NQB]) __attribute__((always_inline)) {
-        const int lo = mykey < kv_len ? (p.causal ? mykey : 0) - q0 - 4 * g : 0x3FFFFFFF;
-        const int hi = N - 1 - q0 - 4 * g;
+        const RangeMask rm(lo_lane - q0, hi_lane - q0);
 #pragma unroll
         for (int sb = 0; sb < NQB; ++sb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int off = 32 * sb + 8 * (r >> 2) + (r & 3);
-            if (off < lo || off > hi) s[sb][r] = kNegInf;
+            if (!rm.keep(off)) s[sb][r] = kNegInf;
           }
       };
 
@@ -1079,12 +1082,11 @@ void bwd_dkdv_pp_kernel(BwdKParams p) {
     auto elements = [&](int t, int j) __attribute__((always_inline)) {
       const int q0 = tile_q0(t);
       if ((p.causal && q0 < kw0 + 31) || (kw0 + 32 > kv_len) || (q0 + BRQ > N)) {
-        const int lo = mykey < kv_len ? (p.causal ? mykey : 0) - q0 - 4 * g : 0x3FFFFFFF;
-        const int hi = N - 1 - q0 - 4 * g;
+        const RangeMask rm(mykey < kv_len ? (p.causal ? mykey : 0) - q0 - 4 * g : 0x3FFFFFFF, N - 1 - q0 - 4 * g);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int off = 8 * (r >> 2) + (r & 3);
-          if (off < lo || off > hi) sacc[r] = kNegInf;
+          if (!rm.keep(off)) sacc[r] = kNegInf;
         }
       }
 #pragma unroll

@@ -376,6 +376,21 @@ struct TileAddr {
   }
 };
 
+// Two-sided element mask with one compare per entry: offsets off (compile-time
+// constants) are kept iff lo <= off <= hi. As unsigned numbers, off - lo <= hi - lo
+// exactly when lo <= off <= hi (for hi >= lo); an empty range becomes one that no
+// offset reaches. Each entry's compare then goes straight to VCC instead of two
+// lane masks per entry held in scalar registers.
+struct RangeMask {
+  uint32_t lo, span;
+  __device__ __forceinline__ RangeMask(int lo_, int hi_) {
+    const bool empty = hi_ < lo_;
+    lo = empty ? 0x40000000u : (uint32_t)lo_;
+    span = empty ? 0u : (uint32_t)(hi_ - lo_);
+  }
+  __device__ __forceinline__ bool keep(int off) const { return (uint32_t)off - lo <= span; }
+};
+
 // Dropout keep bits from Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel
 // Random Numbers: As Easy as 1, 2, 3", SC 2011): 4 x 32-bit counter, 2 x 32-bit
 // key, ten rounds of two 32 x 32 -> 64-bit products mixed by XOR, the key bumped
