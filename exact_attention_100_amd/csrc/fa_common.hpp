@@ -179,10 +179,14 @@ struct TileCopy {
     typedef const void __attribute__((address_space(1)))* gptr;
     typedef void __attribute__((address_space(3)))* lptr;
     const bf16* gt = g + (int64_t)row0 * ld;
+    // (opaque per issue: each copy's LDS destination, the M0 operand, is re-formed from
+    // it by a scalar add instead of being kept in a scalar register across the loop)
+    int wv = wave;
+    asm volatile("" : "+s"(wv));
     if (row0 + ROWS <= nvalid) {
 #pragma unroll
       for (int i = 0; i < PER_WAVE; ++i)
-        __builtin_amdgcn_global_load_lds((gptr)(gt + off[i]), (lptr)(lds_tile + 8 * 64 * (i * NWAVES + wave)),
+        __builtin_amdgcn_global_load_lds((gptr)(gt + off[i]), (lptr)(lds_tile + 8 * 64 * (i * NWAVES + wv)),
                                          16, 0, 0);
     } else {
 #pragma unroll
@@ -191,7 +195,7 @@ struct TileCopy {
         // offset stays within the 32-bit range of off[]).
         const int over = max(row0 + row[i] - (nvalid - 1), 0);
         __builtin_amdgcn_global_load_lds((gptr)(gt + (off[i] - over * (int32_t)ld)),
-                                         (lptr)(lds_tile + 8 * 64 * (i * NWAVES + wave)), 16, 0, 0);
+                                         (lptr)(lds_tile + 8 * 64 * (i * NWAVES + wv)), 16, 0, 0);
       }
     }
   }
