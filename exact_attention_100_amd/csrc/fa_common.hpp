@@ -160,10 +160,11 @@ struct TileCopy {
   static constexpr int CPR = COLS / 8;
   static constexpr int PER_WAVE = ROWS * CPR / (64 * NWAVES);
   static_assert(PER_WAVE >= 1 && PER_WAVE * 64 * NWAVES == ROWS * CPR, "tile must split into whole wave copies");
-  // Row offsets are 32-bit: the API admits row strides below 2^23 elements, so 256 rows at most.
+  // Lane offsets are unsigned 32-bit byte offsets: the API admits row strides below 2^23
+  // elements, so 256 rows at most (255 (2^23 - 16) 2 + 256 bytes < 2^32).
   static_assert(ROWS <= 256, "32-bit lane offsets cover 256 rows of the largest admitted stride");
-  int32_t off[PER_WAVE];  // element offset of this lane's source chunk from the tile's first row
-  int32_t row[PER_WAVE];  // tile row of that chunk
+  uint32_t offb[PER_WAVE];  // byte offset of this lane's source chunk from the tile's first row
+  int32_t row[PER_WAVE];    // tile row of that chunk
   int wave;               // wave index (uniform)
 
   __device__ __forceinline__ void init(int wave_uniform, int lane, int64_t ld) {
@@ -172,7 +173,7 @@ struct TileCopy {
     for (int i = 0; i < PER_WAVE; ++i) {
       const int pch = (i * NWAVES + wave) * 64 + lane;
       row[i] = pch / CPR;
-      off[i] = (int32_t)(row[i] * ld) + 8 * ((pch % CPR) ^ tile_swz<COLS>(row[i]));
+      offb[i] = (uint32_t)(2 * (row[i] * ld + 8 * ((pch % CPR) ^ tile_swz<COLS>(row[i]))));
     }
   }
   __device__ __forceinline__ void issue(bf16* lds_tile, const bf16* g, int64_t ld, int row0, int nvalid) const {
@@ -183,18 +184,20 @@ struct TileCopy {
     // it by a scalar add instead of being kept in a scalar register across the loop)
     int wv = wave;
     asm volatile("" : "+s"(wv));
+    // Each copy addresses a scalar base plus this lane's unsigned 32-bit byte offset (the
+    // saddr form: no vector address arithmetic per copy of a full tile).
+    const char* gb = reinterpret_cast<const char*>(gt);
     if (row0 + ROWS <= nvalid) {
 #pragma unroll
       for (int i = 0; i < PER_WAVE; ++i)
-        __builtin_amdgcn_global_load_lds((gptr)(gt + off[i]), (lptr)(lds_tile + 8 * 64 * (i * NWAVES + wv)),
-                                         16, 0, 0);
+        __builtin_amdgcn_global_load_lds((gptr)(gb + offb[i]), (lptr)(lds_tile + 8 * 64 * (i * NWAVES + wv)), 16, 0, 0);
     } else {
 #pragma unroll
       for (int i = 0; i < PER_WAVE; ++i) {
-        // Step back over rows past nvalid - 1 (at most ROWS of them, so the
-        // offset stays within the 32-bit range of off[]).
+        // Step back over rows past nvalid - 1 (at most row[i] of them, so the offset
+        // stays non-negative and within 32 bits).
         const int over = max(row0 + row[i] - (nvalid - 1), 0);
-        __builtin_amdgcn_global_load_lds((gptr)(gt + (off[i] - over * (int32_t)ld)),
+        __builtin_amdgcn_global_load_lds((gptr)(gb + (offb[i] - (uint32_t)(2 * over * ld))),
                                          (lptr)(lds_tile + 8 * 64 * (i * NWAVES + wv)), 16, 0, 0);
       }
     }
