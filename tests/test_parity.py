@@ -160,6 +160,37 @@ def test_strided_bnhd_layout_matches_contiguous():
         assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_row_stride_at_the_limit(d):
+    """Row strides just below the 2^23 elements the ABI admits, where the tile copies' 32-bit
+    byte offsets are largest (the dK/dV pass copies a 256-row V block at d = 128): the same bits
+    as the contiguous layout. About 34 GB of padded device buffers."""
+    import torch
+    import exact_attention_100_amd as fa
+    N, sn = 256, (1 << 23) - 16
+    case = workloads.make_case(1, 1, N, d, mask="causal", seed=16, name=f"row-stride-limit-d{d}")
+    _say(case.name, "stride_n", sn)
+    t = upload(case)
+
+    def wide(x):
+        w = torch.empty_strided(x.shape, (N * sn, N * sn, sn, 1), dtype=x.dtype, device=x.device)
+        w.copy_(x)
+        return w
+
+    s = {n: wide(t[n]) for n in ("q", "k", "v", "do")}
+    o1, l1 = fa.fwd(t["q"], t["k"], t["v"], causal=True)
+    o2, l2 = fa.fwd(s["q"], s["k"], s["v"], causal=True)
+    g1 = fa.bwd(t["q"], t["k"], t["v"], o1, t["do"], l1, causal=True)
+    g2 = fa.bwd(s["q"], s["k"], s["v"], o2, s["do"], l2, causal=True)
+    torch.cuda.synchronize()
+    assert o2.stride() == (N * sn, N * sn, sn, 1)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
+    del s, o2, g2
+    torch.cuda.empty_cache()
+
+
 def test_deterministic_outputs():
     import torch
     import exact_attention_100_amd as fa
