@@ -398,6 +398,47 @@ struct RangeMask {
   __device__ __forceinline__ bool keep(int off) const { return (uint32_t)off - lo <= span; }
 };
 
+// A wave's 32 x D bf16 output rows through LDS, so that the global stores are whole rows.
+// In the MFMA accumulator layout lane l holds row l % 32 and, for block db and register
+// quad j, the 4 values at columns 32 db + 8 j + 4 (l / 32) (packed in w[db][j]): stored
+// straight to memory, every store instruction writes 8 bytes into each of 32 rows. Here
+// each lane writes its pieces into a wave-private LDS slice (16-byte chunks swizzled by
+// row, so neither the 8-byte writes nor the 16-byte reads meet bank conflicts), then
+// reads back whole 16-byte chunks in row order: each global store covers complete rows
+// (64 lanes x 16 bytes, D / 8 lanes per row). Rows at or past nvalid are not stored.
+// slice: 32 * D * 2 bytes of LDS no other wave touches meanwhile.
+template <int D>
+__device__ __forceinline__ void store_rows_via_lds(bf16* slice, const u32x2 (&w)[D / 32][4], bf16* out, int64_t ld,
+                                                   int row0, int nvalid, int lane) {
+  constexpr int CPR = D / 8;  // 16-byte chunks per row
+  const int r = lane & 31, h = lane >> 5;
+  char* sl = reinterpret_cast<char*>(slice);
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int c = 4 * db + j;
+      *reinterpret_cast<u32x2*>(sl + r * (2 * D) + 16 * (c ^ (r % CPR)) + 8 * h) = w[db][j];
+    }
+  // (the reads below take other lanes' writes: keep them after the writes)
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // Instruction i reads chunk cc of row rr0 + RPI i (RPI = 64 / CPR rows per instruction).
+  constexpr int RPI = 64 / CPR;
+  const int rr0 = lane / CPR, cc = lane % CPR;
+  u32x4 v[CPR / 2];
+#pragma unroll
+  for (int i = 0; i < CPR / 2; ++i) {
+    const int rr = rr0 + RPI * i;
+    v[i] = *reinterpret_cast<const u32x4*>(sl + rr * (2 * D) + 16 * (cc ^ (rr % CPR)));
+  }
+  bf16* o = out + (int64_t)(row0 + rr0) * ld + 8 * cc;
+#pragma unroll
+  for (int i = 0; i < CPR / 2; ++i)
+    if (row0 + rr0 + RPI * i < nvalid) *reinterpret_cast<u32x4*>(o + (int64_t)(RPI * i) * ld) = v[i];
+}
+
 // Dropout keep bits from Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel
 // Random Numbers: As Easy as 1, 2, 3", SC 2011): 4 x 32-bit counter, 2 x 32-bit
 // key, ten rounds of two 32 x 32 -> 64-bit products mixed by XOR, the key bumped

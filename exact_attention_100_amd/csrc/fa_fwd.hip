@@ -707,24 +707,24 @@ void fwd_pp_kernel(FwdKParams p) {
     if (gr == 0) __syncthreads();
   }
 
-  // Epilogue: O = O_acc / l (the rounded weights' sum), LSE = (m + log2 lu) ln 2.
+  // Epilogue: O = O_acc / l (the rounded weights' sum), LSE = (m + log2 lu) ln 2. O goes
+  // out through the tile buffers, free once every wave is past its last read of them.
   const float l_tot = lacc[0];
   const float lu_tot = pair_sum(lu_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  if (qrow < N) {
-    bf16* Orow = static_cast<bf16*>(p.o) + base + (int64_t)qrow * p.sn;
+  u32x2 w[NDB][4];
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+  for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        u32x2 w;
-        w[0] = pack_bf16x2(oacc[db][4 * j + 0] * inv, oacc[db][4 * j + 1] * inv);
-        w[1] = pack_bf16x2(oacc[db][4 * j + 2] * inv, oacc[db][4 * j + 3] * inv);
-        *reinterpret_cast<u32x2*>(Orow + db * 32 + 8 * j + 4 * g) = w;
-      }
-    if (g == 0)
-      p.lse[(int64_t)inst * N + qrow] = lu_tot > 0.f ? (m_run + fast_log2(lu_tot)) * kLn2 : kNegInf;
-  }
+    for (int j = 0; j < 4; ++j) {
+      w[db][j][0] = pack_bf16x2(oacc[db][4 * j + 0] * inv, oacc[db][4 * j + 1] * inv);
+      w[db][j][1] = pack_bf16x2(oacc[db][4 * j + 2] * inv, oacc[db][4 * j + 3] * inv);
+    }
+  static_assert(8 * 32 * D <= 4 * TILE, "eight 32-row slices fit in the tile buffers");
+  __syncthreads();
+  store_rows_via_lds<D>(sT + wave * (32 * D), w, static_cast<bf16*>(p.o) + base, p.sn, wrow0, N, lane);
+  if (qrow < N && g == 0)
+    p.lse[(int64_t)inst * N + qrow] = lu_tot > 0.f ? (m_run + fast_log2(lu_tot)) * kLn2 : kNegInf;
 }
 
 // ------------------------------------------------------------------------------------ f32
