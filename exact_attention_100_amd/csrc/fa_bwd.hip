@@ -1165,21 +1165,33 @@ void bwd_dkdv_pp_kernel(BwdKParams p) {
   }
 
   // dK = scale (dK^T)^T, dV: lane column = mykey, register r = dim 32 db + 8 (r/4) + 4 g + r%4.
-  if (mykey < N) {
-    bf16* dkrow = p.dk + base + (int64_t)mykey * p.sn;
-    bf16* dvrow = p.dv + base + (int64_t)mykey * p.sn;
+  // Both leave through the V block's LDS (free once every wave is past its last read),
+  // one after the other in the same wave-private slice, so that each store writes whole rows.
+  static_assert(8 * 32 * D <= kBwdKeysPP * D, "eight 32-row slices fit in the V block");
+  __syncthreads();
+  bf16* const slice = sV + wave * (32 * D);
+  {
+    u32x2 w[NDB][4];
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        u32x2 wk, wv;
-        wk[0] = pack_bf16x2(dkacc[db][4 * j] * p.scale, dkacc[db][4 * j + 1] * p.scale);
-        wk[1] = pack_bf16x2(dkacc[db][4 * j + 2] * p.scale, dkacc[db][4 * j + 3] * p.scale);
-        wv[0] = pack_bf16x2(dvacc[db][4 * j], dvacc[db][4 * j + 1]);
-        wv[1] = pack_bf16x2(dvacc[db][4 * j + 2], dvacc[db][4 * j + 3]);
-        *reinterpret_cast<u32x2*>(dkrow + db * 32 + 8 * j + 4 * g) = wk;
-        *reinterpret_cast<u32x2*>(dvrow + db * 32 + 8 * j + 4 * g) = wv;
+        w[db][j][0] = pack_bf16x2(dkacc[db][4 * j] * p.scale, dkacc[db][4 * j + 1] * p.scale);
+        w[db][j][1] = pack_bf16x2(dkacc[db][4 * j + 2] * p.scale, dkacc[db][4 * j + 3] * p.scale);
       }
+    store_rows_via_lds<D>(slice, w, p.dk + base, p.sn, kw0, N, lane);
+  }
+  __builtin_amdgcn_wave_barrier();
+  {
+    u32x2 w[NDB][4];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        w[db][j][0] = pack_bf16x2(dvacc[db][4 * j], dvacc[db][4 * j + 1]);
+        w[db][j][1] = pack_bf16x2(dvacc[db][4 * j + 2], dvacc[db][4 * j + 3]);
+      }
+    store_rows_via_lds<D>(slice, w, p.dv + base, p.sn, kw0, N, lane);
   }
 }
 
@@ -1434,19 +1446,20 @@ void bwd_dq_pp_kernel(BwdKParams p) {
     if (gr == 0) __syncthreads();
   }
 
-  // dQ = scale dQ^T^T: lane = query, register r = dim 32 db + 8 (r/4) + 4 g + r%4.
-  if (qrow < N) {
-    bf16* dqrow = p.dq + base + (int64_t)qrow * p.sn;
+  // dQ = scale dQ^T^T: lane = query, register r = dim 32 db + 8 (r/4) + 4 g + r%4; it leaves
+  // through the tile buffers (free once every wave is past its last read) so that each store
+  // writes whole rows.
+  u32x2 w[NDB][4];
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+  for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        u32x2 w;
-        w[0] = pack_bf16x2(dqacc[db][4 * j] * p.scale, dqacc[db][4 * j + 1] * p.scale);
-        w[1] = pack_bf16x2(dqacc[db][4 * j + 2] * p.scale, dqacc[db][4 * j + 3] * p.scale);
-        *reinterpret_cast<u32x2*>(dqrow + db * 32 + 8 * j + 4 * g) = w;
-      }
-  }
+    for (int j = 0; j < 4; ++j) {
+      w[db][j][0] = pack_bf16x2(dqacc[db][4 * j] * p.scale, dqacc[db][4 * j + 1] * p.scale);
+      w[db][j][1] = pack_bf16x2(dqacc[db][4 * j + 2] * p.scale, dqacc[db][4 * j + 3] * p.scale);
+    }
+  static_assert(8 * 32 * D <= 5 * TILE, "eight 32-row slices fit in the tile buffers");
+  __syncthreads();
+  store_rows_via_lds<D>(sT + wave * (32 * D), w, p.dq + base, p.sn, wrow0, N, lane);
 }
 
 // ------------------------------------------------------------------------------ launcher

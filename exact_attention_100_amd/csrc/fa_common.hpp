@@ -411,6 +411,9 @@ template <int D>
 __device__ __forceinline__ void store_rows_via_lds(bf16* slice, const u32x2 (&w)[D / 32][4], bf16* out, int64_t ld,
                                                    int row0, int nvalid, int lane) {
   constexpr int CPR = D / 8;  // 16-byte chunks per row
+  // (opaque: the addresses below are formed here, after the caller's loops, instead of
+  // being hoisted into registers held across them)
+  asm volatile("" : "+v"(lane));
   const int r = lane & 31, h = lane >> 5;
   char* sl = reinterpret_cast<char*>(slice);
 #pragma unroll
