@@ -462,20 +462,22 @@ void fwd_bf16_kernel(FwdKParams p) {
   const float l_tot = lacc[0];
   const float lu_tot = pair_sum(lu_run);
   const float inv = l_tot > 0.f ? (DROP ? p.drop.scale : 1.f) / l_tot : 0.f;
-  if (qrow < N) {
-    bf16* Orow = static_cast<bf16*>(p.o) + base + (int64_t)qrow * p.sn;
+  // O leaves through the tile buffers (free once every wave is past its last read) so that
+  // each store writes whole rows.
+  u32x2 w[NDB][4];
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+  for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        u32x2 w;
-        w[0] = pack_bf16x2(oacc[db][4 * j + 0] * inv, oacc[db][4 * j + 1] * inv);
-        w[1] = pack_bf16x2(oacc[db][4 * j + 2] * inv, oacc[db][4 * j + 3] * inv);
-        *reinterpret_cast<u32x2*>(Orow + db * 32 + 8 * j + 4 * g) = w;
-      }
-    if (g == 0)
-      p.lse[(int64_t)inst * N + qrow] = lu_tot > 0.f ? (m_run + fast_log2(lu_tot)) * kLn2 : kNegInf;
-  }
+    for (int j = 0; j < 4; ++j) {
+      w[db][j][0] = pack_bf16x2(oacc[db][4 * j + 0] * inv, oacc[db][4 * j + 1] * inv);
+      w[db][j][1] = pack_bf16x2(oacc[db][4 * j + 2] * inv, oacc[db][4 * j + 3] * inv);
+    }
+  static_assert(4 * 32 * D <= 4 * TILE, "four 32-row slices fit in the tile buffers");
+  __syncthreads();
+  store_rows_via_lds<D>(sT + uniform_wave_id() * (32 * D), w, static_cast<bf16*>(p.o) + base, p.sn, q0 + 32 * wave,
+                        N, lane);
+  if (qrow < N && g == 0)
+    p.lse[(int64_t)inst * N + qrow] = lu_tot > 0.f ? (m_run + fast_log2(lu_tot)) * kLn2 : kNegInf;
 }
 
 // -------------------------------------------------------------------- bf16, two wave groups
