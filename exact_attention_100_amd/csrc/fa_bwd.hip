@@ -519,8 +519,37 @@ void bwd_dkdv_kernel(BwdKParams p) {
     }
   }
 
-  // dK = scale (dK^T)^T, dV: lane column = mykey, register r = dim 32 db + 8 (r/4) + 4 g + r%4.
-  if (mykey < N) {
+  // dK = scale (dK^T)^T, dV: lane column = mykey, register r = dim 32 db + 8 (r/4) + 4 g + r%4;
+  // with the pipelined tile's single array both leave through LDS, one after the other,
+  // so that each store writes whole rows.
+  if constexpr (PIPE) {
+    static_assert(4 * 32 * D <= 4 * TILE, "four 32-row slices fit in the tile buffers");
+    __syncthreads();
+    bf16* const slice = sT + uniform_wave_id() * (32 * D);
+    {
+      u32x2 w[NDB][4];
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          w[db][j][0] = pack_bf16x2(dkacc[db][4 * j] * p.scale, dkacc[db][4 * j + 1] * p.scale);
+          w[db][j][1] = pack_bf16x2(dkacc[db][4 * j + 2] * p.scale, dkacc[db][4 * j + 3] * p.scale);
+        }
+      store_rows_via_lds<D>(slice, w, p.dk + base, p.sn, kw0, N, lane);
+    }
+    __builtin_amdgcn_wave_barrier();
+    {
+      u32x2 w[NDB][4];
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          w[db][j][0] = pack_bf16x2(dvacc[db][4 * j], dvacc[db][4 * j + 1]);
+          w[db][j][1] = pack_bf16x2(dvacc[db][4 * j + 2], dvacc[db][4 * j + 3]);
+        }
+      store_rows_via_lds<D>(slice, w, p.dv + base, p.sn, kw0, N, lane);
+    }
+  } else if (mykey < N) {
     bf16* dkrow = p.dk + base + (int64_t)mykey * p.sn;
     bf16* dvrow = p.dv + base + (int64_t)mykey * p.sn;
 #pragma unroll
@@ -897,18 +926,26 @@ void bwd_dq_kernel(BwdKParams p) {
     if (t + 1 < n_tiles) iteration(t + 1, bK1, bV1, bK0, bV0);
   }
 
-  // dQ = scale dQ^T^T: lane = query, register r = dim 32 db + 8 (r/4) + 4 g + r%4.
-  if (qrow < N) {
+  // dQ = scale dQ^T^T: lane = query, register r = dim 32 db + 8 (r/4) + 4 g + r%4; with the
+  // pipelined tile's single array it leaves through LDS so that each store writes whole rows.
+  u32x2 w[NDB][4];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      w[db][j][0] = pack_bf16x2(dqacc[db][4 * j] * p.scale, dqacc[db][4 * j + 1] * p.scale);
+      w[db][j][1] = pack_bf16x2(dqacc[db][4 * j + 2] * p.scale, dqacc[db][4 * j + 3] * p.scale);
+    }
+  if constexpr (PIPE) {
+    static_assert(4 * 32 * D <= 4 * TILE, "four 32-row slices fit in the tile buffers");
+    __syncthreads();
+    store_rows_via_lds<D>(sT + uniform_wave_id() * (32 * D), w, p.dq + base, p.sn, q0 + 32 * wave, N, lane);
+  } else if (qrow < N) {
     bf16* dqrow = p.dq + base + (int64_t)qrow * p.sn;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        u32x2 w;
-        w[0] = pack_bf16x2(dqacc[db][4 * j] * p.scale, dqacc[db][4 * j + 1] * p.scale);
-        w[1] = pack_bf16x2(dqacc[db][4 * j + 2] * p.scale, dqacc[db][4 * j + 3] * p.scale);
-        *reinterpret_cast<u32x2*>(dqrow + db * 32 + 8 * j + 4 * g) = w;
-      }
+      for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x2*>(dqrow + db * 32 + 8 * j + 4 * g) = w[db][j];
   }
 }
 
