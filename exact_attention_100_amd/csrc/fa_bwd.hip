@@ -1335,6 +1335,12 @@ void bwd_dq_pp_kernel(BwdKParams p) {
   }
 
   f32x16 sacc[NKB], dpacc[NKB];
+  // Every register of a lane's dP^T block belongs to its own query, so each dP chain starts
+  // from -D instead of zero and the element phase takes dP - D from the products (one VALU
+  // subtraction fewer per pair; measured 1-1.5% off this pass).
+  f32x16 neg_d;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) neg_d[r] = -d_q;
   bf16x8 dsb[2 * NKB];
 
   // Operand ring of the product phases (slot m % (AH + 1) holds product m's operand). A
@@ -1388,7 +1394,7 @@ void bwd_dq_pp_kernel(BwdKParams p) {
         sacc[j / NKK] = mfma_bf16(a, qf[j % NKK], j % NKK == 0 ? f32x16{} : sacc[j / NKK]);
       } else {
         constexpr int j = m - NQ - NS;
-        dpacc[j / NKK] = mfma_bf16(a, df[j % NKK], j % NKK == 0 ? f32x16{} : dpacc[j / NKK]);
+        dpacc[j / NKK] = mfma_bf16(a, df[j % NKK], j % NKK == 0 ? neg_d : dpacc[j / NKK]);
       }
       __builtin_amdgcn_sched_barrier(0);
     });
@@ -1413,7 +1419,7 @@ void bwd_dq_pp_kernel(BwdKParams p) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const float pr = fast_exp2(fmaf(sacc[kb][e], p.c, -lse2_q));
-        dpacc[kb][e] = pr * (dpacc[kb][e] - d_q);
+        dpacc[kb][e] = pr * dpacc[kb][e];  // dP - D: the chain started from -D
       }
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
